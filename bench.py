@@ -1,0 +1,177 @@
+"""Bench: one GPU's share of a Ulysses-4 attention layer at the Wan2.1 shape, on MI355X.
+
+Workload (synthetic, seeded, N(0,1) bf16): global q/k/v [1, 27280, 40, 128]
+cut into 4 rank shards [1, 6820, 40, 128].  One step = the whole hot path
+for one simulated rank's 10 heads: pack (all head groups, one launch) ->
+attention per head group (N = 27280, non-causal, fp32 LSE) -> unpack back
+into the 4 output shards.  Steps cycle over the 4 simulated ranks so the
+repack does not re-read one rank's bytes from cache.
+
+`value` = attention TFLOP/s of the whole step (4*N^2*D*heads per step over
+the step time, pack and unpack included).  The JSON line also carries the
+attention kernel's own rate (`roofline`, HIP events around each launch on the
+launch stream), the repack GB/s, and the CPU oracle timed on a bounded
+sample (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--groups", type=int, default=1, help="head groups per rank (1 = single call, 5 = 2-head groups)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows the oracle computes for cpu_baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(q, k, v, rows_sample: int):
+    """The oracle as it stands (fp64 NumPy), on a bounded sample of the same workload:
+    attention for `rows_sample` query rows of all 10 heads of rank 0 over all 27280 keys."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import layout as olay
+
+    heads = list(range(10))
+    qn = q[:, :, heads].double().numpy()
+    kn = k[:, :, heads].double().numpy()
+    vn = v[:, :, heads].double().numpy()
+    n = qn.shape[1]
+    rows = np.linspace(0, n - 1, rows_sample).astype(np.int64)
+    t0 = time.perf_counter()
+    oatt.attention(qn, kn, vn, oatt.default_scale(128), rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows_sample * n * 128 * len(heads)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy attention, {rows_sample} of 27280 query rows x 10 heads x all 27280 keys "
+                      f"(D=128), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from ulysses_sequence_attention_amd import inputs, ulys
+
+    G = args.groups
+    w = inputs.E2E_P4
+    P, S_l, H, D = w.degree, w.s_local, w.hq, w.head_dim
+    L = ulys.Layout(1, P, S_l, 0, True, H, H, D, G)
+    rows = L.rows
+    gh = L.gq
+    q, k, v = inputs.global_qkv(w)          # CPU bf16 [1, 27280, 40, 128]
+    dev = torch.device("cuda:0")
+    shards = {n: [x[:, p * S_l:(p + 1) * S_l].contiguous().to(dev) for p in range(P)]
+              for n, x in (("q", q), ("k", k), ("v", v))}
+    slot_shape = (G, 1, rows, gh, D)
+    qs = torch.empty(slot_shape, dtype=torch.bfloat16, device=dev)
+    ks = torch.empty_like(qs)
+    vs = torch.empty_like(qs)
+    os_ = torch.empty_like(qs)
+    lse = torch.empty((G, 1, gh, rows), dtype=torch.float32, device=dev)
+    out = [torch.empty_like(s) for s in shards["q"]]
+    stream = torch.cuda.current_stream()
+
+    flops_step = 4.0 * rows * rows * D * (H // P)
+    bytes_pack = 2 * 3 * rows * (H // P) * D * 2       # read + write, q/k/v bf16
+    bytes_unpack = 2 * rows * (H // P) * D * 2
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rank, rec=None):
+        if rec is not None:
+            rec["p0"].record(stream)
+        ulys.ulys_pack(L, rank, -1, shards["q"], shards["k"], shards["v"], qs, ks, vs)
+        if rec is not None:
+            rec["p1"].record(stream)
+        for g in range(G):
+            ulys.ulys_attend_group(qs[g], ks[g], vs[g], os_[g], lse[g])
+        if rec is not None:
+            rec["a1"].record(stream)
+        ulys.ulys_unpack(L, rank, -1, os_, out)
+        if rec is not None:
+            rec["u1"].record(stream)
+
+    for i in range(args.warmup):
+        step(i % P)
+    torch.cuda.synchronize()
+
+    recs = [{k_: ev() for k_ in ("p0", "p1", "a1", "u1")} for _ in range(args.steps)]
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i % P, recs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    pack_ms = sum(r["p0"].elapsed_time(r["p1"]) for r in recs) / args.steps
+    attn_ms = sum(r["p1"].elapsed_time(r["a1"]) for r in recs) / args.steps
+    unpack_ms = sum(r["a1"].elapsed_time(r["u1"]) for r in recs) / args.steps
+    attn_launch_ms = attn_ms / G
+    attn_tflops = flops_step / (attn_ms * 1e-3) / 1e12
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    repack_gbs = (bytes_pack + bytes_unpack) / ((pack_ms + unpack_ms) * 1e-3) / 1e9
+
+    res = {
+        "metric": "attention TFLOP/s + % MFMA peak at N=27280,H=10,D=128 bf16; repack GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": f"Wan2.1 Ulysses-4 share: 4 shards [1,6820,40,128] -> pack 10 heads into {G} "
+                               f"slot(s) [1,27280,{gh},128] -> attention N=27280 D=128 non-causal + LSE -> unpack",
+                   "batch": 1, "seq_len": rows, "heads_per_gpu": H // P, "head_dim": D, "head_groups": G,
+                   "ulysses_degree_simulated": P},
+        "attention_tflops": round(attn_tflops, 2),
+        "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "attention_ms": round(attn_ms, 4),
+        "pack_ms": round(pack_ms, 4),
+        "unpack_ms": round(unpack_ms, 4),
+        "pack_gbs": round(bytes_pack / (pack_ms * 1e-3) / 1e9, 1),
+        "unpack_gbs": round(bytes_unpack / (unpack_ms * 1e-3) / 1e9, 1),
+        "repack_gbs": round(repack_gbs, 1),
+        "repack_frac_hbm_peak": round(repack_gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd_kernel<128,false>",
+                     "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_rows)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

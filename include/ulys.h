@@ -1,0 +1,189 @@
+/*
+ * ulys.h -- C ABI of libulys: one GPU's share of Ulysses sequence-parallel
+ * attention on MI355X (gfx950).
+ *
+ * Three steps make the path, each a call below:
+ *   ulys_pack          shards -> per-head-group receive slots (+ optional e4m3 q/k)
+ *   ulys_attend_group  dense non-causal attention + log-sum-exp on one slot
+ *   ulys_unpack        output slot -> output shards
+ * plus ulys_amax_bf16 (per-tensor fp8 scale source), ulys_strerror and
+ * ulys_last_error.
+ *
+ * Conventions shared by every call
+ *   - Tensors are caller-owned device memory, dense, row-major, with the
+ *     shapes stated per call; bf16 is IEEE bfloat16, fp8 is OCP e4m3fn (one
+ *     byte per element).  Every device pointer must be 16-byte aligned.
+ *   - Arrays of pointers and key gaps are host memory, read only during the
+ *     call; the caller may reuse them on return.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it; none synchronises, allocates, or keeps state between calls.
+ *   - All validation happens before anything is enqueued.  On failure the
+ *     call returns a negative ulys_status, enqueues nothing, and
+ *     ulys_last_error() describes the first violated rule.
+ *   - The all-to-all of the method is modelled as a local permutation: the
+ *     P "shards" below are the P ranks' inputs, all resident on this GPU.
+ *
+ * Glossary: B batch, P Ulysses degree, S_l sharded rows per rank, R
+ * replicated text rows, rows = R + P*S_l, Hq/Hkv model heads, G head groups
+ * per rank, Gq = Hq/(P*G), Gkv = Hkv/(P*G), D head_dim.
+ */
+#ifndef ULYS_H
+#define ULYS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ULYS_OK = 0,
+  ULYS_EINVAL = -1,        /* an argument breaks a rule stated below */
+  ULYS_EUNSUPPORTED = -2,  /* valid but not built: head_dim not 64/128, fp8 V */
+  ULYS_EHIP = -3           /* the HIP runtime refused a launch */
+} ulys_status;
+
+typedef enum {
+  ULYS_BF16 = 0,
+  ULYS_FP8_E4M3 = 1        /* OCP e4m3fn codes, one per-tensor scale each for q and k */
+} ulys_dtype;
+
+/*
+ * Layout of one Ulysses attention call, as every rank sees it.
+ *
+ * Each of the P shards of q (resp. k, v) is [B, R + S_l, Hq (resp. Hkv), D]
+ * bf16.  With R > 0 the replicated rows sit in front of the shard rows when
+ * rep_first = 1 (a replicated prefix) and behind them when rep_first = 0
+ * (a replicated suffix).  Source: sglang multimodal_gen attention layer.py,
+ * USPAttention.forward (num_replicated_prefix / num_replicated_suffix) and
+ * sglang PR #43521 "Layouts" (q/k/v as [batch, s_local, heads, head_dim],
+ * GQA, replicated prefix or suffix).
+ *
+ * Rules (ULYS_EINVAL otherwise): batch, degree, s_local, hq, hkv, groups >= 1;
+ * n_rep >= 0; rep_first in {0, 1}; P | Hq and P | Hkv (flashdreams cp.py,
+ * ContextParallelAttention._impl_ulysses: heads must divide by the CP size);
+ * Hkv | Hq (GQA); G | Hq/P and G | Hkv/P (sglang PR #43521, "Automatic group
+ * count": a group count must divide the q and k/v heads per rank).
+ * head_dim in {64, 128} (ULYS_EUNSUPPORTED otherwise).
+ */
+typedef struct ulys_layout {
+  int32_t batch;
+  int32_t degree;     /* P */
+  int32_t s_local;    /* S_l */
+  int32_t n_rep;      /* R, 0 = no replicated rows */
+  int32_t rep_first;  /* 1 prefix, 0 suffix */
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;   /* D */
+  int32_t groups;     /* G */
+} ulys_layout;
+
+/*
+ * ulys_pack -- fill the receive slots of head group `group` of rank `rank`.
+ *
+ * Source: sglang PR #43521, "Receive slots" (per head group one contiguous
+ * [batch, rows, group_heads, head_dim] tensor in the order attention reads)
+ * and "Layouts" (replicated rows stay out of the exchange; each rank places
+ * its own copy); flashdreams cp.py _impl_ulysses (rank r receives heads
+ * [r*H/P, (r+1)*H/P), sharded rows source-rank-major); sglang layer.py
+ * _forward_with_replicated_prefix (replicated rows sliced to the rank's
+ * heads, q and k/v separately, then joined in front).
+ *
+ *   slot[b, t, j, :] = J_r[b, t, h0 + j, :],  h0 = r*H/P + g*H/(P*G)
+ * where J_r is the joint sequence of rank r: prefix [rep(r) | shard rows of
+ * ranks 0..P-1], suffix [shard rows of ranks 0..P-1 | rep(r)], rep(r) being
+ * shard r's copy of the replicated rows.  Groups take contiguous head blocks.
+ *
+ * q_shards/k_shards/v_shards: host arrays of P device pointers (layout above).
+ * q_slot: [B, rows, Gq, D], k_slot/v_slot: [B, rows, Gkv, D].  group = -1
+ * packs all G groups at once into G consecutive slots ([G][B, rows, Gh, D]).
+ * q_slot and k_slot hold bf16 when qk_dtype = ULYS_BF16 and e4m3fn codes
+ * (1 byte per element) when qk_dtype = ULYS_FP8_E4M3; v_slot is always bf16.
+ *
+ * fp8 (LightX2V PR "Add optimized Ulysses attention path": fp8 payloads
+ * travel with a separate scale): qk_amax is a device pointer to two floats
+ * {max|q|, max|k|} over all shards (ulys_amax_bf16 writes them); the kernel
+ * forms inv = 448 / amax in float32 (1 if amax = 0) and writes
+ * e4m3fn_rne(clamp(float32(x) * inv, -448, 448)).  qk_amax is ignored
+ * (may be NULL) for ULYS_BF16.
+ */
+int ulys_pack(const ulys_layout* layout, int rank, int group,
+              const void* const* q_shards, const void* const* k_shards,
+              const void* const* v_shards,
+              void* q_slot, void* k_slot, void* v_slot,
+              int qk_dtype, const float* qk_amax, void* stream);
+
+/*
+ * ulys_amax_bf16 -- amax_out[0] = max |x| over n_tensors bf16 device arrays
+ * of elems_each elements each (the per-tensor fp8 scale source; exact,
+ * independent of order).  amax_out is a device float, overwritten.
+ * Rules: n_tensors >= 1, every pointer non-NULL and 16-byte aligned,
+ * elems_each a multiple of 8 (ULYS_EINVAL otherwise).
+ */
+int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
+                   float* amax_out, void* stream);
+
+/*
+ * ulys_attend_group -- dense non-causal softmax attention with LSE on one
+ * head group's slots.
+ *
+ * Source: flashdreams cp.py torch_sdpa_cudnn / torch_sdpa_flash (attention
+ * that returns the log-sum-exp); sglang PR #43521 "Receive slots"
+ * (attend(q, k, v) on views of the slot); sglang layer.py LocalAttention
+ * (key mask = zero weight for masked keys; GQA repeats each k/v head
+ * Hq/Hkv times) and USPAttention.forward (a contiguous pad span
+ * [pad_start, pad_end) of masked keys); UlyssesAttention.__init__ (default
+ * scale head_dim^-1/2).
+ *
+ * For each b, q head h (kv head h / (hq/hkv)), row i, over the valid keys J
+ * (those outside [key_gaps[2b], key_gaps[2b+1])):
+ *   s_ij = c * <q_i, k_j>,  o_i = sum_J softmax(s)_ij v_j,  lse_i = ln sum_J exp(s_ij)
+ * c = softmax_scale (<= 0 selects head_dim^-1/2), times q_scale * k_scale
+ * (scale = amax / 448, or 1 if amax = 0, from qk_amax) for fp8 q/k,
+ * all in float32.  Query rows inside the gap are computed like any other
+ * row (the mask is on keys only).
+ *
+ * q: [B, rows, hq, D], k/v: [B, rows, hkv, D]; q/k bf16 or e4m3fn codes
+ * (qk_dtype), v bf16.  o: [B, rows, hq, D] bf16 (round to nearest even).
+ * lse: [B, hq, rows] float32, natural log, or NULL to skip it.
+ * key_gaps: host int32 [B][2] half-open masked key range per batch, or NULL
+ * for none; 0 <= start <= end <= rows and end - start < rows (a batch
+ * without a valid key is ULYS_EINVAL), B <= 256 when given.
+ * Rules: rows >= 1, hq % hkv == 0, head_dim in {64, 128}.  Each head's
+ * result depends only on that head's data: calling on a head subset gives
+ * the same bytes for those heads as the full call.
+ */
+int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
+                      const void* q, const void* k, const void* v, int qk_dtype,
+                      float softmax_scale, const float* qk_amax,
+                      const int32_t* key_gaps, void* o, float* lse, void* stream);
+
+/*
+ * ulys_unpack -- inverse of ulys_pack for the output of (rank, group).
+ *
+ * Source: flashdreams cp.py _impl_ulysses (output all-to-all restores the
+ * sequence shards); sglang layer.py _forward_with_replicated_prefix
+ * (the replicated rows' output is all-gathered over heads, so every rank
+ * gets it) and sglang PR #43521 "Layouts" (output returns in the caller's
+ * row order).
+ *
+ * o_slot: [B, rows, Gq, D] bf16 (group = -1: [G][B, rows, Gq, D]).
+ * o_shards: host array of P device pointers, each [B, R + S_l, Hq, D] bf16;
+ * writes heads h0..h0+Gq of every shard: shard rows of rank p from their
+ * joint rows, replicated rows into every shard.  Other heads are untouched.
+ */
+int ulys_unpack(const ulys_layout* layout, int rank, int group,
+                const void* o_slot, void* const* o_shards, void* stream);
+
+/* Static text for a ulys_status value. */
+const char* ulys_strerror(int status);
+
+/* Text naming the rule the last failed call on this thread broke ("" if none). */
+const char* ulys_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYS_H */

@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: seeded inputs -> oracle and HIP path, comparisons."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention as oatt
+from oracle import fp8 as ofp8
+from oracle import layout as olay
+from ulysses_sequence_attention_amd import inputs
+
+# Tolerances for attention outputs against the fp64 oracle (bf16 o, fp32 lse).
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 1e-3
+LSE_MAX_ABS = 1e-3
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> int16 bit patterns (numpy) for byte-exact work."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy()
+
+
+def f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().cpu().double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def from_bits(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+
+
+def layout_of(w: inputs.Workload):
+    from ulysses_sequence_attention_amd import ulys
+    return ulys.Layout(w.batch, w.degree, w.s_local, w.n_rep, w.rep_first, w.hq, w.hkv, w.head_dim, w.groups)
+
+
+def shards_of(w: inputs.Workload, seed=None):
+    """Seeded global q, k, v and their P shards (CPU bf16 tensors and int16 numpy views)."""
+    q, k, v = inputs.global_qkv(w, seed)
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        out[name] = olay.split_global(bits(x), w.degree, w.n_rep, w.rep_first)
+    return (q, k, v), out
+
+
+def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, label=""):
+    """Assert the bf16 output and fp32 LSE of the GPU are within tolerance of the fp64 oracle.
+
+    ``rows``: the query rows the oracle computed (the GPU arrays hold all rows)."""
+    og = f64(o_gpu)
+    lg = f64(lse_gpu)
+    if rows is not None:
+        og = og[:, rows]
+        lg = lg[:, :, rows]
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), f"{label}: non-finite output"
+    err = np.abs(og - o_ref)
+    lerr = np.abs(lg - lse_ref)
+    stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()))
+    assert stats["o_max"] <= O_MAX_ABS, f"{label}: {stats}"
+    assert stats["o_mean"] <= O_MEAN_ABS, f"{label}: {stats}"
+    assert stats["lse_max"] <= LSE_MAX_ABS, f"{label}: {stats}"
+    return stats
+
+
+def sample_rows(n: int, boundaries=(), every=None, edge=8, extra=64, seed=0):
+    """Deterministic row sample: rows near each boundary, the ends, and a spread."""
+    rs = set(range(min(edge, n))) | set(range(max(0, n - edge), n))
+    for b in boundaries:
+        rs |= set(range(max(0, b - edge), min(n, b + edge)))
+    if every:
+        rs |= set(range(0, n, every))
+    rng = np.random.default_rng(seed)
+    rs |= set(rng.integers(0, n, size=extra).tolist())
+    return np.array(sorted(rs))
+
+
+__all__ = ["oatt", "ofp8", "olay", "inputs", "bits", "f64", "from_bits", "layout_of", "shards_of",
+           "check_attention", "sample_rows"]

@@ -1,0 +1,151 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/ulys.h
+declares, and every invalid call is refused with its status before any HIP call
+(so these run without a GPU; no valid compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulys.h")
+
+
+@pytest.fixture(scope="module")
+def U():
+    lib = os.path.join(ROOT, "ulysses_sequence_attention_amd", "libulys.so")
+    if not os.path.exists(lib):
+        from ulysses_sequence_attention_amd import build
+        build.build()
+    from ulysses_sequence_attention_amd import ulys
+    return ulys
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(ulys_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(U):
+    lib = ctypes.CDLL(U.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(U.EXPORTED)
+
+
+FAKE = 0x10000          # an aligned, never-dereferenced address (calls below fail validation first)
+MIS = 0x10008           # 8-byte aligned only
+
+
+def _arr(n, val=FAKE):
+    a = (ctypes.c_void_p * n)()
+    for i in range(n):
+        a[i] = val
+    return a
+
+
+def _pack(U, L, rank=0, group=0, q=None, k=None, v=None, slots=(FAKE, FAKE, FAKE), dtype=0, amax=FAKE):
+    c = U.Layout(**L).c_struct() if isinstance(L, dict) else L
+    P = c.degree if c.degree > 0 else 1
+    q = _arr(P) if q is None else q
+    k = _arr(P) if k is None else k
+    v = _arr(P) if v is None else v
+    return U.call_raw("ulys_pack", ctypes.byref(c), rank, group, q, k, v, *slots, dtype, amax, None)
+
+
+GOOD = dict(batch=1, degree=4, s_local=10, n_rep=0, rep_first=True, hq=40, hkv=40, head_dim=128, groups=5)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(degree=0), -1), (dict(batch=0), -1), (dict(s_local=0), -1), (dict(groups=0), -1),
+    (dict(n_rep=-1), -1), (dict(hq=42), -1), (dict(hkv=20, hq=40, groups=5), 0),
+    (dict(hkv=12, hq=40), -1), (dict(groups=3), -1), (dict(head_dim=96), -2), (dict(degree=65, hq=65 * 2, hkv=130, groups=1), -1),
+])
+def test_pack_layout_rules(U, change, status):
+    L = dict(GOOD, **change)
+    st = _pack(U, L, group=-2 if status == 0 else 0)   # a valid layout still fails on group -2
+    assert st == (-1 if status == 0 else status), U.last_error()
+    assert U.last_error()
+
+
+def test_pack_rules(U):
+    assert _pack(U, GOOD, rank=4) == -1
+    assert _pack(U, GOOD, rank=-1) == -1
+    assert _pack(U, GOOD, group=5) == -1
+    assert _pack(U, GOOD, dtype=7) == -1
+    assert _pack(U, GOOD, dtype=1, amax=None) == -1                    # fp8 needs amax
+    assert _pack(U, GOOD, q=_arr(4, MIS)) == -1                        # misaligned shard
+    bad = _arr(4)
+    bad[3] = None
+    assert _pack(U, GOOD, k=bad) == -1                                  # NULL shard
+    assert _pack(U, GOOD, slots=(FAKE, None, FAKE)) == -1
+    assert _pack(U, GOOD, slots=(FAKE, FAKE, MIS)) == -1
+    c = U.Layout(**GOOD).c_struct()
+    c.rep_first = 2
+    assert _pack(U, c) == -1
+    assert U.call_raw("ulys_pack", None, 0, 0, _arr(4), _arr(4), _arr(4), FAKE, FAKE, FAKE, 0, None, None) == -1
+    assert "layout" in U.last_error()
+
+
+def _attend(U, batch=1, rows=100, hq=2, hkv=2, d=128, q=FAKE, o=FAKE, dtype=0, scale=0.0, amax=None, gaps=None, lse=None):
+    g = None
+    if gaps is not None:
+        g = (ctypes.c_int32 * len(gaps))(*gaps)
+    return U.call_raw("ulys_attend_group", batch, rows, hq, hkv, d, q, FAKE, FAKE, dtype, ctypes.c_float(scale),
+                      amax, g, o, lse, None)
+
+
+def test_attend_rules(U):
+    assert _attend(U, rows=0) == -1
+    assert _attend(U, batch=0) == -1
+    assert _attend(U, hq=3, hkv=2) == -1
+    assert _attend(U, d=80) == -2
+    assert _attend(U, q=MIS) == -1
+    assert _attend(U, o=None) == -1
+    assert _attend(U, lse=FAKE + 2) == -1
+    assert _attend(U, dtype=1) == -1                                   # fp8 without amax
+    assert _attend(U, scale=float("nan")) == -1
+    assert _attend(U, scale=float("inf")) == -1
+    assert _attend(U, gaps=[5, 3]) == -1                               # end < start
+    assert _attend(U, gaps=[-1, 3]) == -1
+    assert _attend(U, gaps=[90, 101]) == -1                            # past rows
+    assert _attend(U, gaps=[0, 100]) == -1                             # no valid key
+    assert "no valid key" in U.last_error()
+    assert _attend(U, batch=2, gaps=[0, 10, 0, 100]) == -1
+    assert _attend(U, batch=300, gaps=[0, 1] * 300) == -1             # too many gap batches
+
+
+def test_unpack_and_amax_rules(U):
+    c = U.Layout(**GOOD).c_struct()
+    assert U.call_raw("ulys_unpack", ctypes.byref(c), 0, 0, None, _arr(4), None) == -1
+    assert U.call_raw("ulys_unpack", ctypes.byref(c), 0, 0, FAKE, None, None) == -1
+    assert U.call_raw("ulys_unpack", ctypes.byref(c), 9, 0, FAKE, _arr(4), None) == -1
+    c.hq = 41
+    assert U.call_raw("ulys_unpack", ctypes.byref(c), 0, 0, FAKE, _arr(4), None) == -1
+    assert U.call_raw("ulys_amax_bf16", _arr(1), 0, 8, FAKE, None) == -1
+    assert U.call_raw("ulys_amax_bf16", _arr(1), 1, 12, FAKE, None) == -1
+    assert U.call_raw("ulys_amax_bf16", _arr(1), 1, 8, None, None) == -1
+    assert U.call_raw("ulys_amax_bf16", _arr(1, MIS), 1, 8, FAKE, None) == -1
+
+
+def test_strerror(U):
+    lib = ctypes.CDLL(U.LIB_PATH)
+    lib.ulys_strerror.restype = ctypes.c_char_p
+    assert lib.ulys_strerror(0) == b"ok"
+    assert lib.ulys_strerror(-1) == b"invalid argument"
+    assert lib.ulys_strerror(-2) == b"unsupported configuration"
+    assert lib.ulys_strerror(-3) == b"HIP runtime error"
+    assert lib.ulys_strerror(5) == b"unknown status"
+
+
+def test_binding_refuses_cpu_tensors(U):
+    import torch
+    x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        U.ulys_attend_group(x, x, x, x)

@@ -1,0 +1,226 @@
+// libulys C ABI: argument validation and launch geometry (host side).
+//
+// Every rule is checked before anything touches the HIP runtime, so a bad
+// call returns its status with nothing enqueued (and can be exercised on a
+// machine without a GPU).  The library allocates nothing and keeps no state
+// except the per-thread text of the last validation failure.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ulys.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ULYS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Layout rules shared by pack and unpack.
+int check_layout(const ulys_layout* L, int rank, int group) {
+  if (L == nullptr) return fail(ULYS_EINVAL, "layout is NULL");
+  if (L->batch < 1 || L->degree < 1 || L->s_local < 1 || L->hq < 1 || L->hkv < 1 || L->groups < 1)
+    return fail(ULYS_EINVAL, "batch, degree, s_local, hq, hkv and groups must be >= 1");
+  if (L->n_rep < 0) return fail(ULYS_EINVAL, "n_rep must be >= 0");
+  if (L->rep_first != 0 && L->rep_first != 1) return fail(ULYS_EINVAL, "rep_first must be 0 or 1");
+  if (L->degree > ulys::kMaxDegree) return fail(ULYS_EINVAL, "degree %d exceeds %d", L->degree, ulys::kMaxDegree);
+  if (L->hq % L->degree || L->hkv % L->degree)
+    return fail(ULYS_EINVAL, "heads (hq %d, hkv %d) must divide by the Ulysses degree %d", L->hq, L->hkv, L->degree);
+  if (L->hq % L->hkv) return fail(ULYS_EINVAL, "hq %d must be a multiple of hkv %d", L->hq, L->hkv);
+  if ((L->hq / L->degree) % L->groups || (L->hkv / L->degree) % L->groups)
+    return fail(ULYS_EINVAL, "groups %d must divide the q heads (%d) and kv heads (%d) per rank", L->groups,
+                L->hq / L->degree, L->hkv / L->degree);
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(ULYS_EUNSUPPORTED, "head_dim %d not built (64, 128)", L->head_dim);
+  if (rank < 0 || rank >= L->degree) return fail(ULYS_EINVAL, "rank %d outside [0, %d)", rank, L->degree);
+  if (group < -1 || group >= L->groups) return fail(ULYS_EINVAL, "group %d outside [-1, %d)", group, L->groups);
+  const long long rows = (long long)L->n_rep + (long long)L->degree * L->s_local;
+  if (rows > 0x7fffffffLL) return fail(ULYS_EINVAL, "joint rows %lld too large", rows);
+  return ULYS_OK;
+}
+
+int check_ptr_array(const void* const* arr, int n, const char* what) {
+  if (arr == nullptr) return fail(ULYS_EINVAL, "%s pointer array is NULL", what);
+  for (int i = 0; i < n; ++i) {
+    if (arr[i] == nullptr) return fail(ULYS_EINVAL, "%s[%d] is NULL", what, i);
+    if (!aligned16(arr[i])) return fail(ULYS_EINVAL, "%s[%d] is not 16-byte aligned", what, i);
+  }
+  return ULYS_OK;
+}
+
+int check_ptr(const void* p, const char* what) {
+  if (p == nullptr) return fail(ULYS_EINVAL, "%s is NULL", what);
+  if (!aligned16(p)) return fail(ULYS_EINVAL, "%s is not 16-byte aligned", what);
+  return ULYS_OK;
+}
+
+ulys::RepackGeom geom_of(const ulys_layout* L, int rank, int group) {
+  ulys::RepackGeom g;
+  g.batch = L->batch;
+  g.degree = L->degree;
+  g.s_local = L->s_local;
+  g.n_rep = L->n_rep;
+  g.rep_first = L->rep_first;
+  g.rank = rank;
+  g.rows = L->n_rep + L->degree * L->s_local;
+  g.shard_rows = L->n_rep + L->s_local;
+  g.head_dim = L->head_dim;
+  g.ngroups = group < 0 ? L->groups : 1;
+  return g;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(ULYS_EHIP, "HIP: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ulys_pack(const ulys_layout* L, int rank, int group, const void* const* q_shards,
+              const void* const* k_shards, const void* const* v_shards, void* q_slot, void* k_slot,
+              void* v_slot, int qk_dtype, const float* qk_amax, void* stream) {
+  int st = check_layout(L, rank, group);
+  if (st) return st;
+  if (qk_dtype != ULYS_BF16 && qk_dtype != ULYS_FP8_E4M3) return fail(ULYS_EINVAL, "qk_dtype %d unknown", qk_dtype);
+  if ((st = check_ptr_array(q_shards, L->degree, "q_shards"))) return st;
+  if ((st = check_ptr_array(k_shards, L->degree, "k_shards"))) return st;
+  if ((st = check_ptr_array(v_shards, L->degree, "v_shards"))) return st;
+  if ((st = check_ptr(q_slot, "q_slot"))) return st;
+  if ((st = check_ptr(k_slot, "k_slot"))) return st;
+  if ((st = check_ptr(v_slot, "v_slot"))) return st;
+  const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
+  if (fp8 && qk_amax == nullptr) return fail(ULYS_EINVAL, "qk_amax is NULL with fp8 q/k");
+  if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
+
+  ulys::PackArgs a;
+  memset(&a, 0, sizeof a);
+  a.g = geom_of(L, rank, group);
+  const int heads[3] = {L->hq, L->hkv, L->hkv};
+  const void* const* src[3] = {q_shards, k_shards, v_shards};
+  void* dst[3] = {q_slot, k_slot, v_slot};
+  const int g0 = group < 0 ? 0 : group;
+  for (int t = 0; t < 3; ++t) {
+    for (int p = 0; p < L->degree; ++p) a.src[t][p] = (const uint16_t*)src[t][p];
+    a.dst[t] = dst[t];
+    a.heads[t] = heads[t];
+    a.gh[t] = heads[t] / L->degree / L->groups;
+    a.h0[t] = rank * (heads[t] / L->degree) + g0 * a.gh[t];
+    a.fp8[t] = (fp8 && t < 2) ? 1 : 0;
+  }
+  a.amax = qk_amax;
+  return hip_status(ulys::launch_pack(a, (hipStream_t)stream));
+}
+
+int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each, float* amax_out, void* stream) {
+  if (n_tensors < 1 || n_tensors > ulys::kMaxAmaxTensors)
+    return fail(ULYS_EINVAL, "n_tensors %d outside [1, %d]", n_tensors, ulys::kMaxAmaxTensors);
+  int st = check_ptr_array(tensors, n_tensors, "tensors");
+  if (st) return st;
+  if (elems_each % 8) return fail(ULYS_EINVAL, "elems_each %zu is not a multiple of 8", elems_each);
+  if (amax_out == nullptr) return fail(ULYS_EINVAL, "amax_out is NULL");
+  if ((uintptr_t)amax_out & 3u) return fail(ULYS_EINVAL, "amax_out is not 4-byte aligned");
+  ulys::AmaxArgs a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < n_tensors; ++i) a.src[i] = (const uint16_t*)tensors[i];
+  a.n = n_tensors;
+  a.chunks_each = elems_each / 8;
+  a.out = (unsigned int*)amax_out;
+  return hip_status(ulys::launch_amax(a, (hipStream_t)stream));
+}
+
+int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
+                      const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
+                      const int32_t* key_gaps, void* o, float* lse, void* stream) {
+  if (batch < 1 || rows < 1 || hq < 1 || hkv < 1)
+    return fail(ULYS_EINVAL, "batch, rows, hq and hkv must be >= 1");
+  if (hq % hkv) return fail(ULYS_EINVAL, "hq %d must be a multiple of hkv %d", hq, hkv);
+  if (head_dim != 64 && head_dim != 128) return fail(ULYS_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
+  if (qk_dtype != ULYS_BF16 && qk_dtype != ULYS_FP8_E4M3) return fail(ULYS_EINVAL, "qk_dtype %d unknown", qk_dtype);
+  if (batch > 65535 || hq > 65535) return fail(ULYS_EINVAL, "batch and hq must be <= 65535");
+  if ((long long)batch * rows * hq * head_dim > (1LL << 40)) return fail(ULYS_EINVAL, "tensor too large");
+  int st;
+  if ((st = check_ptr(q, "q"))) return st;
+  if ((st = check_ptr(k, "k"))) return st;
+  if ((st = check_ptr(v, "v"))) return st;
+  if ((st = check_ptr(o, "o"))) return st;
+  if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(ULYS_EINVAL, "lse is not 4-byte aligned");
+  const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
+  if (fp8 && qk_amax == nullptr) return fail(ULYS_EINVAL, "qk_amax is NULL with fp8 q/k");
+  if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(ULYS_EINVAL, "softmax_scale must be finite");
+
+  ulys::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  if (key_gaps != nullptr) {
+    if (batch > ulys::kMaxGapBatch) return fail(ULYS_EINVAL, "key gaps for batch %d > %d", batch, ulys::kMaxGapBatch);
+    for (int b = 0; b < batch; ++b) {
+      const int g0 = key_gaps[2 * b], g1 = key_gaps[2 * b + 1];
+      if (g0 < 0 || g1 < g0 || g1 > rows)
+        return fail(ULYS_EINVAL, "key gap [%d, %d) of batch %d outside [0, %d]", g0, g1, b, rows);
+      if (g1 - g0 >= rows) return fail(ULYS_EINVAL, "batch %d has no valid key", b);
+      a.gap[b][0] = g0;
+      a.gap[b][1] = g1;
+    }
+    a.has_gap = 1;
+  }
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.amax = qk_amax;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+  a.batch = batch;
+  a.rows = rows;
+  a.hq = hq;
+  a.hkv = hkv;
+  return hip_status(ulys::launch_attn(a, head_dim, fp8, (hipStream_t)stream));
+}
+
+int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, void* const* o_shards, void* stream) {
+  int st = check_layout(L, rank, group);
+  if (st) return st;
+  if ((st = check_ptr(o_slot, "o_slot"))) return st;
+  if ((st = check_ptr_array((const void* const*)o_shards, L->degree, "o_shards"))) return st;
+  ulys::UnpackArgs a;
+  memset(&a, 0, sizeof a);
+  a.g = geom_of(L, rank, group);
+  a.src = (const uint16_t*)o_slot;
+  for (int p = 0; p < L->degree; ++p) a.dst[p] = (uint16_t*)o_shards[p];
+  a.heads = L->hq;
+  a.gh = L->hq / L->degree / L->groups;
+  a.h0 = rank * (L->hq / L->degree) + (group < 0 ? 0 : group) * a.gh;
+  return hip_status(ulys::launch_unpack(a, (hipStream_t)stream));
+}
+
+const char* ulys_strerror(int status) {
+  switch (status) {
+    case ULYS_OK: return "ok";
+    case ULYS_EINVAL: return "invalid argument";
+    case ULYS_EUNSUPPORTED: return "unsupported configuration";
+    case ULYS_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ulys_last_error(void) { return g_last_error; }
+
+}  // extern "C"

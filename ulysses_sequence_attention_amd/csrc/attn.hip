@@ -1,0 +1,370 @@
+// Dense non-causal attention with log-sum-exp for one head group, gfx950.
+//
+// What it computes (sglang layer.py LocalAttention / USPAttention.forward;
+// flashdreams cp.py torch_sdpa_*): per (b, q head h, row i), over the keys J
+// outside the batch's masked gap, s_ij = c <q_i, k_j>, o_i = softmax(s_i) V,
+// lse_i = ln sum_J exp(s_ij); kv head = h / (hq / hkv) (GQA).
+//
+// How (MI355X-first):
+//  * One workgroup = 4 waves = 256 query rows of one (b, h); each wave owns 64
+//    rows as two 32-row MFMA blocks, so every K/V fragment read from LDS feeds
+//    two MFMAs (halves LDS read traffic per flop against 32-row waves).
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+//    (or the fp8 v_mfma_scale_f32_32x32x64_f8f6f4 for e4m3 q/k): in the
+//    accumulator every lane then holds ONE query row and 16 keys, so row max
+//    and row sum are in-lane reductions plus one exchange with lane^32, and
+//    the softmax probabilities are already laid out as the B operand of the
+//    O^T = V^T P^T MFMA (no shuffles between the two contractions).
+//  * K tiles sit row-major in LDS with a 16-byte XOR swizzle; V tiles are
+//    stored transposed (V^T, keys contiguous per head-dim row) with the key
+//    order permuted to match the probability registers, so each MFMA operand
+//    is one conflict-free 16-byte LDS read.
+//  * 64-key tiles, double-buffered: the next tile's global loads are in
+//    flight while the current tile is computed; one barrier per tile.
+//  * Online softmax in the exp2 domain with a lazy max: the running max is
+//    only raised (and O, l rescaled) when a tile's max exceeds it by more than
+//    2^8, a wave-uniform branch; probabilities stay <= 256, exact either way
+//    because the final normalisation divides by the sum built with the same
+//    max.  Row sums add the bf16-rounded probabilities that feed the MFMA.
+//  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
+//    that straddle the gap are masked per element.
+// A head's arithmetic never depends on the other heads of the call, the grid
+// or the slot strides, so a head-group split reproduces the full call's bytes.
+#include "internal.h"
+
+namespace ulys {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 64;
+constexpr int kBM = kWaves * kRowsPerWave;   // 256 query rows per workgroup
+constexpr int kBN = 64;                      // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
+
+template <int D, bool FP8>
+struct Cfg {
+  static constexpr int kQKBytes = FP8 ? 1 : 2;
+  static constexpr int kKRow = D * kQKBytes;            // bytes per K row in LDS
+  static constexpr int kKChunks = kKRow / 16;           // 16-byte chunks per K row
+  static constexpr int kKSwz = kKChunks < 8 ? kKChunks : 8;
+  static constexpr int kKTile = kBN * kKRow;            // bytes
+  static constexpr int kVTile = D * kBN * 2;            // bytes (V^T, bf16)
+  static constexpr int kKLoads = kKTile / 16 / kThreads; // 16-byte loads per thread
+  static constexpr int kVLoads = kVTile / 16 / kThreads;
+  static constexpr int kQKSteps = FP8 ? D / 64 : D / 16; // MFMAs along head_dim per 32x32 block
+  static constexpr int kDB = D / 32;                     // 32-wide head_dim blocks of O
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+
+// key position inside a 16-key group: swap bits 2 and 3, so that the 8 keys a
+// lane contributes to one PV MFMA (see accumulator layout) are contiguous.
+__device__ __forceinline__ int vpos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D, bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_kernel(AttnArgs a) {
+  using C = Cfg<D, FP8>;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][C::kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][C::kVTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int qtile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int b = blockIdx.z;
+  const int rows = a.rows;
+  const int kvh = head / (a.hq / a.hkv);
+
+  float c = a.scale;
+  if (FP8) {
+    const float aq = a.amax[0], ak = a.amax[1];
+    const float sq = aq > 0.0f ? __fdiv_rn(aq, 448.0f) : 1.0f;
+    const float sk = ak > 0.0f ? __fdiv_rn(ak, 448.0f) : 1.0f;
+    c = (c * sq) * sk;
+  }
+  const float c2 = c * kLog2e;
+
+  // ---- key range: skip tiles wholly inside the gap ----
+  const int ntiles = (rows + kBN - 1) / kBN;
+  int gs = rows, ge = rows;   // empty gap
+  if (a.has_gap) { gs = a.gap[b][0]; ge = a.gap[b][1]; if (ge <= gs) { gs = rows; ge = rows; } }
+  const int skip_first = (gs + kBN - 1) / kBN;
+  const int skip_last = (ge >= rows) ? ntiles : ge / kBN;   // tiles [skip_first, skip_last) are fully masked
+  auto next_tile = [&](int j) {
+    const int n = j + 1;
+    return (n == skip_first && skip_last > n) ? skip_last : n;
+  };
+  const int first_tile = (skip_first == 0 && skip_last > 0) ? skip_last : 0;
+
+  // ---- Q fragments in registers (B operand of S^T = K Q^T) ----
+  const size_t q_row_stride = (size_t)a.hq * D;            // elements
+  const size_t kv_row_stride = (size_t)a.hkv * D;
+  const int qrow0 = qtile * kBM + wave * kRowsPerWave;
+  constexpr int kQRegs = FP8 ? 8 : 4;                       // dwords per fragment
+  unsigned int qf[2][C::kQKSteps][kQRegs];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = qrow0 + rb * 32 + l32;
+    const unsigned char* qp = (const unsigned char*)a.q +
+        (((size_t)b * rows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
+#pragma unroll
+    for (int kk = 0; kk < C::kQKSteps; ++kk) {
+      const int off = FP8 ? (kk * 64 + hh * 32) : (kk * 16 + hh * 8) * 2;   // bytes
+#pragma unroll
+      for (int part = 0; part < kQRegs / 4; ++part) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < rows) x = ld16(qp + off + part * 16);
+        qf[rb][kk][part * 4 + 0] = x.x; qf[rb][kk][part * 4 + 1] = x.y;
+        qf[rb][kk][part * 4 + 2] = x.z; qf[rb][kk][part * 4 + 3] = x.w;
+      }
+    }
+  }
+
+  // ---- global -> register -> LDS staging of one K/V tile ----
+  const unsigned char* kbase = (const unsigned char*)a.k + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * C::kQKBytes;
+  const unsigned char* vbase = (const unsigned char*)a.v + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * 2;
+  u32x4 kreg[C::kKLoads];
+  u32x4 vreg[C::kVLoads];
+  auto load_tile = [&](int j) {
+    const int k0 = j * kBN;
+#pragma unroll
+    for (int u = 0; u < C::kKLoads; ++u) {
+      const int cid = tid + u * kThreads;
+      const int key = cid / C::kKChunks, ck = cid % C::kKChunks;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (k0 + key < rows) x = ld16(kbase + ((size_t)(k0 + key) * kv_row_stride) * C::kQKBytes + ck * 16);
+      kreg[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < C::kVLoads; ++u) {
+      const int cid = tid + u * kThreads;
+      const int key = cid % kBN, dc = cid / kBN;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (k0 + key < rows) x = ld16(vbase + ((size_t)(k0 + key) * kv_row_stride) * 2 + dc * 16);
+      vreg[u] = x;
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int u = 0; u < C::kKLoads; ++u) {
+      const int cid = tid + u * kThreads;
+      const int key = cid / C::kKChunks, ck = cid % C::kKChunks;
+      const int sck = ck ^ (key & (C::kKSwz - 1));
+      *(u32x4*)(&k_lds[stage][key * C::kKRow + sck * 16]) = kreg[u];
+    }
+    unsigned short* vt = (unsigned short*)v_lds[stage];
+#pragma unroll
+    for (int u = 0; u < C::kVLoads; ++u) {
+      const int cid = tid + u * kThreads;
+      const int key = cid % kBN, dc = cid / kBN;
+      const int pos = vpos(key);
+      const unsigned int w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int d = dc * 8 + i;
+        const int col = (((pos >> 3) ^ (d & 7)) << 3) | (pos & 7);
+        vt[d * kBN + col] = (unsigned short)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
+      }
+    }
+  };
+
+  // ---- running state ----
+  f32x16 o[2][C::kDB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.0f;
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max of c*log2e*s (lazy)
+  float l_run[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};   // partial row sums (two chains)
+
+  load_tile(first_tile);
+  store_tile(0);
+  __syncthreads();
+
+  int stage = 0;
+  for (int j = first_tile; j < ntiles;) {
+    const int jn = next_tile(j);
+    if (jn < ntiles) load_tile(jn);
+    const int k0 = j * kBN;
+
+    const unsigned short* vt = (const unsigned short*)v_lds[stage];
+    // Each 32-key block of the tile is one online-softmax step.
+#pragma unroll 1
+    for (int kb = 0; kb < 2; ++kb) {
+      // ---- S^T = K Q^T for 32 keys x 64 rows ----
+      f32x16 s[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[rb][r] = 0.0f;
+      const int key = kb * 32 + l32;
+      const unsigned char* krow = &k_lds[stage][key * C::kKRow];
+#pragma unroll
+      for (int kk = 0; kk < C::kQKSteps; ++kk) {
+        if constexpr (!FP8) {
+          const int ck = (kk * 2 + hh) ^ (key & (C::kKSwz - 1));
+          const u32x4 kx = *(const u32x4*)(krow + ck * 16);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, kx);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const u32x4 qx = {qf[rb][kk][0], qf[rb][kk][1], qf[rb][kk][2], qf[rb][kk][3]};
+            s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, qx), s[rb], 0, 0, 0);
+          }
+        } else {
+          const int ck0 = (kk * 4 + hh * 2) ^ (key & (C::kKSwz - 1));
+          const int ck1 = (kk * 4 + hh * 2 + 1) ^ (key & (C::kKSwz - 1));
+          const u32x4 k0x = *(const u32x4*)(krow + ck0 * 16);
+          const u32x4 k1x = *(const u32x4*)(krow + ck1 * 16);
+          const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
+                            (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const i32x8 bq = {(int)qf[rb][kk][0], (int)qf[rb][kk][1], (int)qf[rb][kk][2], (int)qf[rb][kk][3],
+                              (int)qf[rb][kk][4], (int)qf[rb][kk][5], (int)qf[rb][kk][6], (int)qf[rb][kk][7]};
+            s[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s[rb], 0, 0, 0, 127, 0, 127);
+          }
+        }
+      }
+
+      // ---- mask: tail keys and keys inside the gap ----
+      const int kb0 = k0 + kb * 32;
+      if (kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = kb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (kidx >= rows || (kidx >= gs && kidx < ge)) { s[0][r] = -INFINITY; s[1][r] = -INFINITY; }
+        }
+      }
+
+      // ---- online softmax (exp2 domain, lazy max) ----
+      float mx[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float m = s[rb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[rb][r]);
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        mx[rb] = m * c2;
+      }
+      const bool need = (mx[0] > m_run[0] + kLazy) || (mx[1] > m_run[1] + kLazy);
+      if (__any(need)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mn = fmaxf(m_run[rb], mx[rb]);
+          const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
+          m_run[rb] = mn;
+          l_run[rb][0] *= alpha;
+          l_run[rb][1] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+        }
+      }
+
+      // probabilities -> bf16 B operands of the PV MFMA: p[rb][e] holds
+      // accumulator registers 8e..8e+7 of s[rb]
+      bf16x8 p[2][2];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mb = (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * e + 2 * i], c2, -mb));
+            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * e + 2 * i + 1], c2, -mb));
+            const f32x2 xx = {x0, x1};
+            const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
+            p[rb][e][2 * i] = pk[0];
+            p[rb][e][2 * i + 1] = pk[1];
+            l_run[rb][i & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run[rb][i & 1], false);
+          }
+      }
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        const int d = db * 32 + l32;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int grp = (2 * (2 * kb + e) + hh) ^ (d & 7);
+          const u32x4 vx = *(const u32x4*)(vt + d * kBN + grp * 8);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, vx);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[rb][e], o[rb][db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (jn < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+    j = jn;
+  }
+
+  // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = qrow0 + rb * 32 + l32;
+    float l = l_run[rb][0] + l_run[rb][1];
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    if (row < rows) {
+      uint16_t* op = a.o + ((size_t)b * rows + row) * q_row_stride + (size_t)head * D;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x2 lo = {o[rb][db][4 * r4 + 0] * inv, o[rb][db][4 * r4 + 1] * inv};
+          const f32x2 hi = {o[rb][db][4 * r4 + 2] * inv, o[rb][db][4 * r4 + 3] * inv};
+          const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
+          const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
+          u32x2 w;
+          w.x = __builtin_bit_cast(unsigned int, blo);
+          w.y = __builtin_bit_cast(unsigned int, bhi);
+          *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
+        }
+      if (a.lse != nullptr && hh == 0)
+        a.lse[((size_t)b * a.hq + head) * rows + row] = (m_run[rb] + __log2f(l)) * kLn2;
+    }
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.rows + kBM - 1) / kBM, a.hq, a.batch);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, hipStream_t s) {
+  if (head_dim == 128) return fp8 ? launch<128, true>(a, s) : launch<128, false>(a, s);
+  return fp8 ? launch<64, true>(a, s) : launch<64, false>(a, s);
+}
+
+}  // namespace ulys

@@ -1,0 +1,63 @@
+// Internal declarations shared by the libulys translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ulys {
+
+constexpr int kMaxDegree = 64;      // P shards per call (kernel-argument arrays)
+constexpr int kMaxGapBatch = 256;   // batches that may carry a key gap
+constexpr int kMaxAmaxTensors = 64;
+
+// Geometry of one pack/unpack launch, resolved on the host.
+struct RepackGeom {
+  int batch, rows, s_local, n_rep, rep_first, rank, degree, shard_rows, head_dim;
+  int ngroups;   // groups handled by this launch (1, or all G)
+};
+
+struct PackArgs {
+  RepackGeom g;
+  const uint16_t* src[3][kMaxDegree];  // q, k, v shards
+  void* dst[3];                        // q, k, v slots
+  int heads[3];                        // heads of the source tensor (Hq, Hkv, Hkv)
+  int gh[3];                           // heads per group
+  int h0[3];                           // first head of the first group of this launch
+  int fp8[3];                          // 1: cast to e4m3fn (q, k only)
+  const float* amax;                   // device {amax_q, amax_k} when fp8
+};
+
+struct UnpackArgs {
+  RepackGeom g;
+  const uint16_t* src;                 // o slot(s)
+  uint16_t* dst[kMaxDegree];           // o shards
+  int heads, gh, h0;
+};
+
+struct AmaxArgs {
+  const uint16_t* src[kMaxAmaxTensors];
+  int n;
+  size_t chunks_each;                  // 16-byte chunks per tensor
+  unsigned int* out;                   // float bits of max |x|
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  uint16_t* o;
+  float* lse;
+  const float* amax;                   // fp8 q/k: device {amax_q, amax_k}
+  float scale;                         // softmax scale (before fp8 descale)
+  int batch, rows, hq, hkv;
+  int has_gap;
+  int gap[kMaxGapBatch][2];
+};
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);
+hipError_t launch_amax(const AmaxArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, hipStream_t s);
+
+}  // namespace ulys

@@ -1,0 +1,211 @@
+"""Python binding of libulys (argument marshalling only).
+
+Each function has the name of the C entry point it wraps and does nothing
+but check tensor dtypes/devices/sizes, collect raw device pointers and the
+current HIP stream, call the library, and turn a negative status into an
+exception (ValueError for ULYS_EINVAL, NotImplementedError for
+ULYS_EUNSUPPORTED, RuntimeError for ULYS_EHIP).  Every step of the path runs
+in the library's HIP kernels; there is no other implementation here.
+Importing this module fails loudly if libulys.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libulys.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ulysses_sequence_attention_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ULYS_OK, ULYS_EINVAL, ULYS_EUNSUPPORTED, ULYS_EHIP = 0, -1, -2, -3
+ULYS_BF16, ULYS_FP8_E4M3 = 0, 1
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class ulys_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "degree", "s_local", "n_rep", "rep_first", "hq", "hkv", "head_dim", "groups")]
+
+
+_lib.ulys_pack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                           ctypes.POINTER(_vp), _vp, _vp, _vp, _i, _vp, _vp]
+_lib.ulys_pack.restype = _i
+_lib.ulys_amax_bf16.argtypes = [ctypes.POINTER(_vp), _i, ctypes.c_size_t, _vp, _vp]
+_lib.ulys_amax_bf16.restype = _i
+_lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
+                                   ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
+_lib.ulys_attend_group.restype = _i
+_lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.POINTER(_vp), _vp]
+_lib.ulys_unpack.restype = _i
+_lib.ulys_strerror.argtypes = [_i]
+_lib.ulys_strerror.restype = ctypes.c_char_p
+_lib.ulys_last_error.argtypes = []
+_lib.ulys_last_error.restype = ctypes.c_char_p
+
+EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_strerror", "ulys_last_error")
+
+
+@dataclass(frozen=True)
+class Layout:
+    """Python mirror of ``ulys_layout``."""
+    batch: int
+    degree: int
+    s_local: int
+    n_rep: int
+    rep_first: bool
+    hq: int
+    hkv: int
+    head_dim: int
+    groups: int
+
+    @property
+    def rows(self) -> int:
+        return self.n_rep + self.degree * self.s_local
+
+    @property
+    def shard_rows(self) -> int:
+        return self.n_rep + self.s_local
+
+    @property
+    def gq(self) -> int:
+        return self.hq // self.degree // self.groups
+
+    @property
+    def gkv(self) -> int:
+        return self.hkv // self.degree // self.groups
+
+    def c_struct(self) -> ulys_layout:
+        return ulys_layout(self.batch, self.degree, self.s_local, self.n_rep, int(self.rep_first), self.hq, self.hkv,
+                           self.head_dim, self.groups)
+
+
+def _check(status: int) -> None:
+    if status == ULYS_OK:
+        return
+    msg = f"{_lib.ulys_strerror(status).decode()}: {_lib.ulys_last_error().decode()}"
+    if status == ULYS_EINVAL:
+        raise ValueError(msg)
+    if status == ULYS_EUNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, numel: int | None = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _ptrs(ts, name, dtypes, numel):
+    arr = (_vp * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _dev(t, f"{name}[{i}]", dtypes, numel)
+    return arr
+
+
+_BF16 = (torch.bfloat16,)
+_QK8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def ulys_pack(layout: Layout, rank: int, group: int, q_shards, k_shards, v_shards, q_slot, k_slot, v_slot,
+              qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None, stream=None) -> None:
+    """Fill the receive slots of (rank, group); group = -1 packs all groups."""
+    L = layout
+    if len(q_shards) != L.degree or len(k_shards) != L.degree or len(v_shards) != L.degree:
+        raise ValueError("need one shard per rank for q, k and v")
+    ng = L.groups if group < 0 else 1
+    nq = L.batch * L.shard_rows * L.hq * L.head_dim
+    nkv = L.batch * L.shard_rows * L.hkv * L.head_dim
+    qa = _ptrs(q_shards, "q_shards", _BF16, nq)
+    ka = _ptrs(k_shards, "k_shards", _BF16, nkv)
+    va = _ptrs(v_shards, "v_shards", _BF16, nkv)
+    qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
+    qs = _dev(q_slot, "q_slot", qk_t, ng * L.batch * L.rows * L.gq * L.head_dim)
+    ks = _dev(k_slot, "k_slot", qk_t, ng * L.batch * L.rows * L.gkv * L.head_dim)
+    vs = _dev(v_slot, "v_slot", _BF16, ng * L.batch * L.rows * L.gkv * L.head_dim)
+    am = None
+    if qk_amax is not None:
+        am = _dev(qk_amax, "qk_amax", (torch.float32,), 2)
+    c = L.c_struct()
+    _check(_lib.ulys_pack(ctypes.byref(c), rank, group, qa, ka, va, qs, ks, vs, qk_dtype, am, _stream(stream)))
+
+
+def ulys_amax_bf16(tensors, out: torch.Tensor, stream=None) -> None:
+    """out[0] = max |x| over all ``tensors`` (bf16, same element count)."""
+    n = tensors[0].numel()
+    arr = _ptrs(tensors, "tensors", _BF16, n)
+    o = _dev(out, "out", (torch.float32,))
+    _check(_lib.ulys_amax_bf16(arr, len(tensors), n, o, _stream(stream)))
+
+
+def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                      lse: torch.Tensor | None = None, softmax_scale: float = 0.0,
+                      key_gaps=None, qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None,
+                      stream=None) -> None:
+    """Attention on one slot: q ``[B, rows, hq, D]``, k/v ``[B, rows, hkv, D]`` -> o (and lse ``[B, hq, rows]``).
+
+    ``key_gaps``: per-batch ``(start, end)`` masked key ranges, or None.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
+    b, rows, hq, d = q.shape
+    hkv = k.shape[2]
+    if tuple(k.shape) != (b, rows, hkv, d) or tuple(v.shape) != (b, rows, hkv, d) or tuple(o.shape) != (b, rows, hq, d):
+        raise ValueError("shape mismatch between q, k, v and o")
+    qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
+    qp = _dev(q, "q", qk_t)
+    kp = _dev(k, "k", qk_t)
+    vp = _dev(v, "v", _BF16)
+    op = _dev(o, "o", _BF16)
+    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), b * hq * rows)
+    am = None if qk_amax is None else _dev(qk_amax, "qk_amax", (torch.float32,), 2)
+    gaps = None
+    if key_gaps is not None:
+        if len(key_gaps) != b:
+            raise ValueError("key_gaps needs one (start, end) per batch")
+        gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
+    _check(_lib.ulys_attend_group(b, rows, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, op, lp,
+                                  _stream(stream)))
+
+
+def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_shards, stream=None) -> None:
+    """Scatter the output slot(s) of (rank, group) into the P output shards."""
+    L = layout
+    if len(o_shards) != L.degree:
+        raise ValueError("need one output shard per rank")
+    ng = L.groups if group < 0 else 1
+    sp = _dev(o_slot, "o_slot", _BF16, ng * L.batch * L.rows * L.gq * L.head_dim)
+    oa = _ptrs(o_shards, "o_shards", _BF16, L.batch * L.shard_rows * L.hq * L.head_dim)
+    c = L.c_struct()
+    _check(_lib.ulys_unpack(ctypes.byref(c), rank, group, sp, oa, _stream(stream)))
+
+
+def call_raw(name: str, *args) -> int:
+    """Call an entry point with raw ctypes arguments and return its status (for ABI tests)."""
+    return getattr(_lib, name)(*args)
+
+
+def last_error() -> str:
+    return _lib.ulys_last_error().decode()
