@@ -15,17 +15,19 @@
 //    and row sum are in-lane reductions plus one exchange with lane^32, and
 //    the softmax probabilities are already laid out as the B operand of the
 //    O^T = V^T P^T MFMA (no shuffles between the two contractions).
-//  * K tiles sit row-major in LDS with a 16-byte XOR swizzle; V tiles are
-//    stored transposed (V^T, keys contiguous per head-dim row) with the key
-//    order permuted to match the probability registers, so each MFMA operand
-//    is one conflict-free 16-byte LDS read.
+//  * K and V tiles sit row-major in LDS (XOR-swizzled in 16- and 8-byte
+//    chunks).  K fragments are plain 16-byte reads; V^T fragments come from
+//    gfx950's transposing LDS read (ds_read_b64_tr_b16: within 16 lanes, four
+//    8-byte row pieces are returned as columns), so V is never transposed in
+//    registers or written element by element.
 //  * 64-key tiles, double-buffered: the next tile's global loads are in
 //    flight while the current tile is computed; one barrier per tile.
 //  * Online softmax in the exp2 domain with a lazy max: the running max is
 //    only raised (and O, l rescaled) when a tile's max exceeds it by more than
 //    2^8, a wave-uniform branch; probabilities stay <= 256, exact either way
 //    because the final normalisation divides by the sum built with the same
-//    max.  Row sums add the bf16-rounded probabilities that feed the MFMA.
+//    max.  Row sums are fp32 sums of the unrounded probabilities (the LSE
+//    must not inherit the 2^-9 bf16 rounding of the MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
 // A head's arithmetic never depends on the other heads of the call, the grid
@@ -57,9 +59,11 @@ struct Cfg {
   static constexpr int kQKBytes = FP8 ? 1 : 2;
   static constexpr int kKRow = D * kQKBytes;            // bytes per K row in LDS
   static constexpr int kKChunks = kKRow / 16;           // 16-byte chunks per K row
-  static constexpr int kKSwz = kKChunks < 8 ? kKChunks : 8;
+  static constexpr int kKSwz = kKChunks < 16 ? kKChunks : 16;
+  static constexpr int kVRow = D * 2;                   // bytes per V row in LDS
+  static constexpr int kVChunks = kVRow / 16;
   static constexpr int kKTile = kBN * kKRow;            // bytes
-  static constexpr int kVTile = D * kBN * 2;            // bytes (V^T, bf16)
+  static constexpr int kVTile = kBN * kVRow;            // bytes (bf16)
   static constexpr int kKLoads = kKTile / 16 / kThreads; // 16-byte loads per thread
   static constexpr int kVLoads = kVTile / 16 / kThreads;
   static constexpr int kQKSteps = FP8 ? D / 64 : D / 16; // MFMAs along head_dim per 32x32 block
@@ -68,10 +72,21 @@ struct Cfg {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
-// key position inside a 16-key group: swap bits 2 and 3, so that the 8 keys a
-// lane contributes to one PV MFMA (see accumulator layout) are contiguous.
-__device__ __forceinline__ int vpos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// 8-byte chunk index of V row `key` after the swizzle: rows read together by a
+// transposing LDS read land on distinct banks.
+template <int D>
+__device__ __forceinline__ int vswz(int key, int chunk8) {
+  return chunk8 ^ (D == 128 ? ((key & 3) << 3) : (((key >> 1) & 1) << 3));
+}
+
+__device__ __forceinline__ float lane_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, bool FP8>
@@ -156,9 +171,9 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < C::kVLoads; ++u) {
       const int cid = tid + u * kThreads;
-      const int key = cid % kBN, dc = cid / kBN;
+      const int key = cid / C::kVChunks, ck = cid % C::kVChunks;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (k0 + key < rows) x = ld16(vbase + ((size_t)(k0 + key) * kv_row_stride) * 2 + dc * 16);
+      if (k0 + key < rows) x = ld16(vbase + ((size_t)(k0 + key) * kv_row_stride) * 2 + ck * 16);
       vreg[u] = x;
     }
   };
@@ -170,19 +185,11 @@ void attn_fwd_kernel(AttnArgs a) {
       const int sck = ck ^ (key & (C::kKSwz - 1));
       *(u32x4*)(&k_lds[stage][key * C::kKRow + sck * 16]) = kreg[u];
     }
-    unsigned short* vt = (unsigned short*)v_lds[stage];
 #pragma unroll
     for (int u = 0; u < C::kVLoads; ++u) {
       const int cid = tid + u * kThreads;
-      const int key = cid % kBN, dc = cid / kBN;
-      const int pos = vpos(key);
-      const unsigned int w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = dc * 8 + i;
-        const int col = (((pos >> 3) ^ (d & 7)) << 3) | (pos & 7);
-        vt[d * kBN + col] = (unsigned short)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
-      }
+      const int key = cid / C::kVChunks, ck = cid % C::kVChunks;
+      *(u32x4*)(&v_lds[stage][key * C::kVRow + vswz<D>(key, 2 * ck) * 8]) = vreg[u];
     }
   };
 
@@ -207,7 +214,6 @@ void attn_fwd_kernel(AttnArgs a) {
     if (jn < ntiles) load_tile(jn);
     const int k0 = j * kBN;
 
-    const unsigned short* vt = (const unsigned short*)v_lds[stage];
     // Each 32-key block of the tile is one online-softmax step.
 #pragma unroll 1
     for (int kb = 0; kb < 2; ++kb) {
@@ -263,7 +269,7 @@ void attn_fwd_kernel(AttnArgs a) {
         float m = s[rb][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) m = fmaxf(m, s[rb][r]);
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        m = lane_swap_max(m);
         mx[rb] = m * c2;
       }
       const bool need = (mx[0] > m_run[0] + kLazy) || (mx[1] > m_run[1] + kLazy);
@@ -285,7 +291,6 @@ void attn_fwd_kernel(AttnArgs a) {
       // probabilities -> bf16 B operands of the PV MFMA: p[rb][e] holds
       // accumulator registers 8e..8e+7 of s[rb]
       bf16x8 p[2][2];
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const float mb = (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb];
@@ -299,19 +304,28 @@ void attn_fwd_kernel(AttnArgs a) {
             const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
             p[rb][e][2 * i] = pk[0];
             p[rb][e][2 * i + 1] = pk[1];
-            l_run[rb][i & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run[rb][i & 1], false);
+            l_run[rb][0] += x0;
+            l_run[rb][1] += x1;
           }
       }
 
       // ---- O^T += V^T P^T ----
+      // A operand of lane l: V[key(hh, i)][d = 32 db + l%32], i = 0..7, read as two
+      // transposing 8-byte loads over keys base + 4 hh + (0..3) and base + 8 + 4 hh + (0..3).
+      const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
-        const int d = db * 32 + l32;
+        const int chunk8 = db * 8 + (g16 & 1) * 4 + tcol;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int grp = (2 * (2 * kb + e) + hh) ^ (d & 7);
-          const u32x4 vx = *(const u32x4*)(vt + d * kBN + grp * 8);
-          const bf16x8 af = __builtin_bit_cast(bf16x8, vx);
+          const int key_a = kb * 32 + 16 * e + 4 * (g16 >> 1) + jrow;
+          const int key_b = key_a + 8;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_a * C::kVRow + vswz<D>(key_a, chunk8) * 8]));
+          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_b * C::kVRow + vswz<D>(key_b, chunk8) * 8]));
+          const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[rb][e], o[rb][db], 0, 0, 0);
@@ -329,8 +343,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int row = qrow0 + rb * 32 + l32;
-    float l = l_run[rb][0] + l_run[rb][1];
-    l += __shfl_xor(l, 32, 64);
+    const float l = lane_swap_sum(l_run[rb][0] + l_run[rb][1]);
     const float inv = 1.0f / l;
     if (row < rows) {
       uint16_t* op = a.o + ((size_t)b * rows + row) * q_row_stride + (size_t)head * D;
