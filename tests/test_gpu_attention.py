@@ -63,6 +63,17 @@ def test_ragged_masked_gqa(gpu, b, rows, hq, hkv, d, gaps):
     check_attention(o, l, o_ref, l_ref, label=f"b{b} n{rows} h{hq}/{hkv} d{d} gaps {gaps}")
 
 
+@pytest.mark.parametrize("gap", [(5, 6), (31, 33), (32, 64), (63, 65), (100, 300), (0, 1), (449, 450),
+                                 (200, 450), (1, 450)])
+def test_gap_edges(gpu, gap):
+    """Masked key ranges that start/end inside, on and across 32-key blocks and 64-key tiles."""
+    w = inputs.small("gapedge", 70, s_local=450, hq=2, hkv=1, head_dim=128, q_mult=2.0)
+    q, k, v = [bits(x) for x in inputs.global_qkv(w)]
+    o, l = _attend(gpu, from_bits(q), from_bits(k), from_bits(v), gaps=[gap])
+    o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(128), [gap])
+    check_attention(o, l, o_ref, l_ref, label=f"gap {gap}")
+
+
 def test_masked_kv_contents_do_not_matter(gpu):
     """Masked keys get zero weight: replacing their K/V by +-1e4 leaves o and lse bit-identical."""
     w = inputs.small("adv", 50, s_local=900, hq=2, hkv=2, head_dim=128)

@@ -6,28 +6,31 @@
 // lse_i = ln sum_J exp(s_ij); kv head = h / (hq / hkv) (GQA).
 //
 // How (MI355X-first):
-//  * One workgroup = 4 waves = 256 query rows of one (b, h); each wave owns 64
-//    rows as two 32-row MFMA blocks, so every K/V fragment read from LDS feeds
-//    two MFMAs (halves LDS read traffic per flop against 32-row waves).
+//  * One workgroup = 256 query rows of one (b, h), split over the waves in
+//    32-row MFMA blocks (RB blocks per wave).  All waves share the K/V tiles
+//    in LDS.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (or the fp8 v_mfma_scale_f32_32x32x64_f8f6f4 for e4m3 q/k): in the
 //    accumulator every lane then holds ONE query row and 16 keys, so row max
-//    and row sum are in-lane reductions plus one exchange with lane^32, and
-//    the softmax probabilities are already laid out as the B operand of the
-//    O^T = V^T P^T MFMA (no shuffles between the two contractions).
+//    and row sum are in-lane reductions plus one exchange with lane^32
+//    (v_permlane32_swap), and the softmax probabilities are already laid out
+//    as the B operand of the O^T = V^T P^T MFMA (no shuffles between the two
+//    contractions).
 //  * K and V tiles sit row-major in LDS (XOR-swizzled in 16- and 8-byte
 //    chunks).  K fragments are plain 16-byte reads; V^T fragments come from
 //    gfx950's transposing LDS read (ds_read_b64_tr_b16: within 16 lanes, four
 //    8-byte row pieces are returned as columns), so V is never transposed in
 //    registers or written element by element.
-//  * 64-key tiles, double-buffered: the next tile's global loads are in
-//    flight while the current tile is computed; one barrier per tile.
-//  * Online softmax in the exp2 domain with a lazy max: the running max is
-//    only raised (and O, l rescaled) when a tile's max exceeds it by more than
-//    2^8, a wave-uniform branch; probabilities stay <= 256, exact either way
-//    because the final normalisation divides by the sum built with the same
-//    max.  Row sums are fp32 sums of the unrounded probabilities (the LSE
-//    must not inherit the 2^-9 bf16 rounding of the MFMA operand).
+//  * 64-key tiles, double-buffered in LDS and filled by direct global->LDS
+//    16-byte loads (no staging registers): the next tile streams in while
+//    the current one is computed; one barrier per tile.
+//  * Online softmax in the exp2 domain per 32-key block with a lazy max: the
+//    running max is only raised (and O, l rescaled) when a block's max
+//    exceeds it by more than 2^8, a wave-uniform branch; probabilities stay
+//    <= 256, exact either way because the final normalisation divides by the
+//    sum built with the same max.  Row sums are fp32 sums of the unrounded
+//    probabilities (the LSE must not inherit the 2^-9 bf16 rounding of the
+//    MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
 // A head's arithmetic never depends on the other heads of the call, the grid
@@ -38,6 +41,7 @@ namespace ulys {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -45,17 +49,20 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 64;
-constexpr int kBM = kWaves * kRowsPerWave;   // 256 query rows per workgroup
-constexpr int kBN = 64;                      // keys per tile
+constexpr int kBM = 256;                     // query rows per workgroup
+constexpr int kBN = 64;                      // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
 
-template <int D, bool FP8>
+#ifndef ULYS_ATTN_RB
+#define ULYS_ATTN_RB 1                       // 32-row MFMA blocks per wave
+#endif
+
+template <int D, bool FP8, int RB>
 struct Cfg {
+  static constexpr int kWaves = kBM / (32 * RB);
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kQKBytes = FP8 ? 1 : 2;
   static constexpr int kKRow = D * kQKBytes;            // bytes per K row in LDS
   static constexpr int kKChunks = kKRow / 16;           // 16-byte chunks per K row
@@ -64,10 +71,12 @@ struct Cfg {
   static constexpr int kVChunks = kVRow / 16;
   static constexpr int kKTile = kBN * kKRow;            // bytes
   static constexpr int kVTile = kBN * kVRow;            // bytes (bf16)
-  static constexpr int kKLoads = kKTile / 16 / kThreads; // 16-byte loads per thread
-  static constexpr int kVLoads = kVTile / 16 / kThreads;
   static constexpr int kQKSteps = FP8 ? D / 64 : D / 16; // MFMAs along head_dim per 32x32 block
   static constexpr int kDB = D / 32;                     // 32-wide head_dim blocks of O
+  static constexpr int kKSegs = kKTile / 1024;          // 1 KB LDS segments per tile
+  static constexpr int kVSegs = kVTile / 1024;
+  static constexpr int kKSegsPerWave = (kKSegs + kWaves - 1) / kWaves;
+  static constexpr int kVSegsPerWave = (kVSegs + kWaves - 1) / kWaves;
 };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
@@ -89,10 +98,11 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+template <int D, bool FP8, int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, FP8, RB>::kThreads, Cfg<D, FP8, RB>::kThreads),
+                          amdgpu_waves_per_eu(Cfg<D, FP8, RB>::kWaves / 4, Cfg<D, FP8, RB>::kWaves / 4)))
 void attn_fwd_kernel(AttnArgs a) {
-  using C = Cfg<D, FP8>;
+  using C = Cfg<D, FP8, RB>;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][C::kKTile];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][C::kVTile];
 
@@ -132,11 +142,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- Q fragments in registers (B operand of S^T = K Q^T) ----
   const size_t q_row_stride = (size_t)a.hq * D;            // elements
   const size_t kv_row_stride = (size_t)a.hkv * D;
-  const int qrow0 = qtile * kBM + wave * kRowsPerWave;
+  const int qrow0 = qtile * kBM + wave * (32 * RB);
   constexpr int kQRegs = FP8 ? 8 : 4;                       // dwords per fragment
-  unsigned int qf[2][C::kQKSteps][kQRegs];
+  unsigned int qf[RB][C::kQKSteps][kQRegs];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int row = qrow0 + rb * 32 + l32;
     const unsigned char* qp = (const unsigned char*)a.q +
         (((size_t)b * rows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
@@ -153,74 +163,76 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  // ---- global -> register -> LDS staging of one K/V tile ----
+  // ---- global -> LDS staging of one K/V tile (direct 16-byte loads) ----
+  // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i, so each
+  // instruction fills one contiguous 1 KB segment; a lane picks the global chunk
+  // that belongs at its LDS position under the XOR swizzle.  Rows past the end
+  // are clamped to the last row (their scores are masked, their V is finite).
   const unsigned char* kbase = (const unsigned char*)a.k + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * C::kQKBytes;
   const unsigned char* vbase = (const unsigned char*)a.v + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * 2;
-  u32x4 kreg[C::kKLoads];
-  u32x4 vreg[C::kVLoads];
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j, int stage) {
     const int k0 = j * kBN;
+    constexpr int kKRowsPerSeg = 1024 / C::kKRow;
 #pragma unroll
-    for (int u = 0; u < C::kKLoads; ++u) {
-      const int cid = tid + u * kThreads;
-      const int key = cid / C::kKChunks, ck = cid % C::kKChunks;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (k0 + key < rows) x = ld16(kbase + ((size_t)(k0 + key) * kv_row_stride) * C::kQKBytes + ck * 16);
-      kreg[u] = x;
+    for (int u = 0; u < C::kKSegsPerWave; ++u) {
+      const int seg = wave + u * C::kWaves;
+      if (C::kKSegs % C::kWaves != 0 && seg >= C::kKSegs) break;   // wave-uniform
+      const int key = seg * kKRowsPerSeg + lane / C::kKChunks;
+      const int sck = lane % C::kKChunks;
+      const int ck = sck ^ (key & (C::kKSwz - 1));
+      const int grow = min(k0 + key, rows - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + (size_t)grow * kv_row_stride * C::kQKBytes + ck * 16),
+          (void __attribute__((address_space(3)))*)(&k_lds[stage][seg * 1024]), 16, 0, 0);
     }
+    constexpr int kVRowsPerSeg = 1024 / C::kVRow;
 #pragma unroll
-    for (int u = 0; u < C::kVLoads; ++u) {
-      const int cid = tid + u * kThreads;
-      const int key = cid / C::kVChunks, ck = cid % C::kVChunks;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (k0 + key < rows) x = ld16(vbase + ((size_t)(k0 + key) * kv_row_stride) * 2 + ck * 16);
-      vreg[u] = x;
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int u = 0; u < C::kKLoads; ++u) {
-      const int cid = tid + u * kThreads;
-      const int key = cid / C::kKChunks, ck = cid % C::kKChunks;
-      const int sck = ck ^ (key & (C::kKSwz - 1));
-      *(u32x4*)(&k_lds[stage][key * C::kKRow + sck * 16]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::kVLoads; ++u) {
-      const int cid = tid + u * kThreads;
-      const int key = cid / C::kVChunks, ck = cid % C::kVChunks;
-      *(u32x4*)(&v_lds[stage][key * C::kVRow + vswz<D>(key, 2 * ck) * 8]) = vreg[u];
+    for (int u = 0; u < C::kVSegsPerWave; ++u) {
+      const int seg = wave + u * C::kWaves;
+      if (C::kVSegs % C::kWaves != 0 && seg >= C::kVSegs) break;   // wave-uniform
+      const int key = seg * kVRowsPerSeg + lane / C::kVChunks;
+      const int sck = lane % C::kVChunks;                 // 16-byte slot in the LDS row
+      const int ck = vswz<D>(key, 2 * sck) >> 1;          // its global 16-byte chunk
+      const int grow = min(k0 + key, rows - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vbase + (size_t)grow * kv_row_stride * 2 + ck * 16),
+          (void __attribute__((address_space(3)))*)(&v_lds[stage][seg * 1024]), 16, 0, 0);
     }
   };
 
   // ---- running state ----
-  f32x16 o[2][C::kDB];
+  f32x16 o[RB][C::kDB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.0f;
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max of c*log2e*s (lazy)
-  float l_run[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};   // partial row sums (two chains)
+  float m_run[RB];          // running max of c*log2e*s (lazy)
+  float l_run[RB][2];       // partial row sums (two chains)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb][0] = 0.0f; l_run[rb][1] = 0.0f; }
 
-  load_tile(first_tile);
-  store_tile(0);
+  load_tile(first_tile, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+
+  // lanes' roles in the transposing V reads (see the PV step)
+  const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
 
   int stage = 0;
   for (int j = first_tile; j < ntiles;) {
     const int jn = next_tile(j);
-    if (jn < ntiles) load_tile(jn);
+    if (jn < ntiles) load_tile(jn, stage ^ 1);
     const int k0 = j * kBN;
 
     // Each 32-key block of the tile is one online-softmax step.
 #pragma unroll 1
     for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T for 32 keys x 64 rows ----
-      f32x16 s[2];
+      // ---- S^T = K Q^T for 32 keys x 32*RB rows ----
+      f32x16 s[RB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[rb][r] = 0.0f;
       const int key = kb * 32 + l32;
@@ -232,7 +244,7 @@ void attn_fwd_kernel(AttnArgs a) {
           const u32x4 kx = *(const u32x4*)(krow + ck * 16);
           const bf16x8 af = __builtin_bit_cast(bf16x8, kx);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
+          for (int rb = 0; rb < RB; ++rb) {
             const u32x4 qx = {qf[rb][kk][0], qf[rb][kk][1], qf[rb][kk][2], qf[rb][kk][3]};
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, qx), s[rb], 0, 0, 0);
           }
@@ -244,7 +256,7 @@ void attn_fwd_kernel(AttnArgs a) {
           const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
                             (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
+          for (int rb = 0; rb < RB; ++rb) {
             const i32x8 bq = {(int)qf[rb][kk][0], (int)qf[rb][kk][1], (int)qf[rb][kk][2], (int)qf[rb][kk][3],
                               (int)qf[rb][kk][4], (int)qf[rb][kk][5], (int)qf[rb][kk][6], (int)qf[rb][kk][7]};
             s[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s[rb], 0, 0, 0, 127, 0, 127);
@@ -253,29 +265,35 @@ void attn_fwd_kernel(AttnArgs a) {
       }
 
       // ---- mask: tail keys and keys inside the gap ----
+      // Branch-free selects per register (the key of register r is
+      // kb0 + 8 (r / 4) + 4 hh + r % 4), under one wave-uniform branch.
       const int kb0 = k0 + kb * 32;
       if (kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs)) {
+        const int kl = kb0 + 4 * hh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kidx = kb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (kidx >= rows || (kidx >= gs && kidx < ge)) { s[0][r] = -INFINITY; s[1][r] = -INFINITY; }
+          const int kidx = kl + 8 * (r >> 2) + (r & 3);
+          const bool dead = (kidx >= rows) | ((kidx >= gs) & (kidx < ge));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[rb][r] = dead ? -INFINITY : s[rb][r];
         }
       }
 
       // ---- online softmax (exp2 domain, lazy max) ----
-      float mx[2];
+      float mx[RB];
+      bool need = false;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         float m = s[rb][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) m = fmaxf(m, s[rb][r]);
         m = lane_swap_max(m);
         mx[rb] = m * c2;
+        need = need || (mx[rb] > m_run[rb] + kLazy);
       }
-      const bool need = (mx[0] > m_run[0] + kLazy) || (mx[1] > m_run[1] + kLazy);
       if (__any(need)) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
           const float mn = fmaxf(m_run[rb], mx[rb]);
           const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
           m_run[rb] = mn;
@@ -290,9 +308,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
       // probabilities -> bf16 B operands of the PV MFMA: p[rb][e] holds
       // accumulator registers 8e..8e+7 of s[rb]
-      bf16x8 p[2][2];
+      bf16x8 p[RB][2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         const float mb = (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb];
 #pragma unroll
         for (int e = 0; e < 2; ++e)
@@ -312,7 +330,6 @@ void attn_fwd_kernel(AttnArgs a) {
       // ---- O^T += V^T P^T ----
       // A operand of lane l: V[key(hh, i)][d = 32 db + l%32], i = 0..7, read as two
       // transposing 8-byte loads over keys base + 4 hh + (0..3) and base + 8 + 4 hh + (0..3).
-      const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
         const int chunk8 = db * 8 + (g16 & 1) * 4 + tcol;
@@ -320,20 +337,19 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int e = 0; e < 2; ++e) {
           const int key_a = kb * 32 + 16 * e + 4 * (g16 >> 1) + jrow;
           const int key_b = key_a + 8;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
               (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_a * C::kVRow + vswz<D>(key_a, chunk8) * 8]));
           const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
               (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_b * C::kVRow + vswz<D>(key_b, chunk8) * 8]));
           const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[rb][e], o[rb][db], 0, 0, 0);
         }
       }
     }
 
-    if (jn < ntiles) store_tile(stage ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     stage ^= 1;
     j = jn;
@@ -341,7 +357,7 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int row = qrow0 + rb * 32 + l32;
     const float l = lane_swap_sum(l_run[rb][0] + l_run[rb][1]);
     const float inv = 1.0f / l;
@@ -368,8 +384,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool FP8>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
+  using C = Cfg<D, FP8, ULYS_ATTN_RB>;
   dim3 grid((a.rows + kBM - 1) / kBM, a.hq, a.batch);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, ULYS_ATTN_RB>), grid, dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
