@@ -81,6 +81,9 @@ struct Cfg {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
+template <int S>
+struct StageTag { static constexpr int value = S; };
+
 // 8-byte chunk index of V row `key` after the swizzle: rows read together by a
 // transposing LDS read land on distinct banks.
 template <int D>
@@ -103,8 +106,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, FP8, RB>::kThreads,
                           amdgpu_waves_per_eu(Cfg<D, FP8, RB>::kWaves / 4, Cfg<D, FP8, RB>::kWaves / 4)))
 void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, FP8, RB>;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][C::kKTile];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][C::kVTile];
+  // One LDS array per stage, selected at compile time: the compiler can then
+  // prove that the DMA filling one stage never aliases reads of the other and
+  // does not wait for in-flight tile loads before every LDS read.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[C::kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::kVTile];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[C::kVTile];
+  auto k_of = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return k_lds0; else return k_lds1; };
+  auto v_of = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return v_lds0; else return v_lds1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,7 +180,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // are clamped to the last row (their scores are masked, their V is finite).
   const unsigned char* kbase = (const unsigned char*)a.k + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * C::kQKBytes;
   const unsigned char* vbase = (const unsigned char*)a.v + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * 2;
-  auto load_tile = [&](int j, int stage) {
+  auto load_tile = [&](int j, auto st) {
+    unsigned char* kl = k_of(st);
+    unsigned char* vl = v_of(st);
     const int k0 = j * kBN;
     constexpr int kKRowsPerSeg = 1024 / C::kKRow;
 #pragma unroll
@@ -183,7 +195,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const int grow = min(k0 + key, rows - 1);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(kbase + (size_t)grow * kv_row_stride * C::kQKBytes + ck * 16),
-          (void __attribute__((address_space(3)))*)(&k_lds[stage][seg * 1024]), 16, 0, 0);
+          (void __attribute__((address_space(3)))*)(&kl[seg * 1024]), 16, 0, 0);
     }
     constexpr int kVRowsPerSeg = 1024 / C::kVRow;
 #pragma unroll
@@ -196,7 +208,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const int grow = min(k0 + key, rows - 1);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(vbase + (size_t)grow * kv_row_stride * 2 + ck * 16),
-          (void __attribute__((address_space(3)))*)(&v_lds[stage][seg * 1024]), 16, 0, 0);
+          (void __attribute__((address_space(3)))*)(&vl[seg * 1024]), 16, 0, 0);
     }
   };
 
@@ -213,17 +225,26 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb][0] = 0.0f; l_run[rb][1] = 0.0f; }
 
-  load_tile(first_tile, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // End of a tile: this wave's tile loads have landed and its LDS reads are
+  // done (s_waitcnt vmcnt(0) lgkmcnt(0), as a builtin so the compiler's own
+  // wait tracking knows), then all waves meet at s_barrier.  The empty asm
+  // statements keep the compiler from moving memory accesses across it.
+  auto tile_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  load_tile(first_tile, StageTag<0>{});
+  tile_barrier();
 
   // lanes' roles in the transposing V reads (see the PV step)
   const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
 
-  int stage = 0;
-  for (int j = first_tile; j < ntiles;) {
-    const int jn = next_tile(j);
-    if (jn < ntiles) load_tile(jn, stage ^ 1);
+  auto compute_tile = [&](int j, auto st) {
+    const unsigned char* kl = k_of(st);
+    const unsigned char* vl = v_of(st);
     const int k0 = j * kBN;
 
     // Each 32-key block of the tile is one online-softmax step.
@@ -236,7 +257,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[rb][r] = 0.0f;
       const int key = kb * 32 + l32;
-      const unsigned char* krow = &k_lds[stage][key * C::kKRow];
+      const unsigned char* krow = &kl[key * C::kKRow];
 #pragma unroll
       for (int kk = 0; kk < C::kQKSteps; ++kk) {
         if constexpr (!FP8) {
@@ -338,9 +359,9 @@ void attn_fwd_kernel(AttnArgs a) {
           const int key_a = kb * 32 + 16 * e + 4 * (g16 >> 1) + jrow;
           const int key_b = key_a + 8;
           const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_a * C::kVRow + vswz<D>(key_a, chunk8) * 8]));
+              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(&vl[key_a * C::kVRow + vswz<D>(key_a, chunk8) * 8]));
           const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&v_lds[stage][key_b * C::kVRow + vswz<D>(key_b, chunk8) * 8]));
+              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(&vl[key_b * C::kVRow + vswz<D>(key_b, chunk8) * 8]));
           const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
@@ -349,9 +370,22 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    stage ^= 1;
+  };
+
+  // Tiles alternate between the two stages; the next tile's loads are issued
+  // before the current tile is computed.
+  for (int j = first_tile;;) {
+    int jn = next_tile(j);
+    if (jn < ntiles) load_tile(jn, StageTag<1>{});
+    compute_tile(j, StageTag<0>{});
+    tile_barrier();
+    if (jn >= ntiles) break;
+    j = jn;
+    jn = next_tile(j);
+    if (jn < ntiles) load_tile(jn, StageTag<0>{});
+    compute_tile(j, StageTag<1>{});
+    tile_barrier();
+    if (jn >= ntiles) break;
     j = jn;
   }
 
