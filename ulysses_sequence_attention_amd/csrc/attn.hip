@@ -239,8 +239,30 @@ void attn_fwd_kernel(AttnArgs a) {
   load_tile(first_tile, StageTag<0>{});
   tile_barrier();
 
-  // lanes' roles in the transposing V reads (see the PV step)
+  // Per-lane LDS byte offsets of the MFMA operand reads, computed once: the
+  // XOR swizzles only involve key bits that are the same for every 32-key
+  // block, so each read is a base register plus a compile-time offset.
+  //  K (A operand of S^T): lane row l32, head-dim chunk(s) of step kk.
+  constexpr int kKOffs = FP8 ? 2 * C::kQKSteps : C::kQKSteps;
+  int koff[kKOffs];
+#pragma unroll
+  for (int kk = 0; kk < C::kQKSteps; ++kk) {
+    const int sw = l32 & (C::kKSwz - 1);
+    if constexpr (!FP8) {
+      koff[kk] = l32 * C::kKRow + (((kk * 2 + hh) ^ sw) * 16);
+    } else {
+      koff[2 * kk] = l32 * C::kKRow + (((kk * 4 + hh * 2) ^ sw) * 16);
+      koff[2 * kk + 1] = l32 * C::kKRow + (((kk * 4 + hh * 2 + 1) ^ sw) * 16);
+    }
+  }
+  //  V (A operand of O^T, transposing reads): within 16 lanes, lane 4j+t reads
+  //  row key0 + j at head-dim d0 + 4t.. (see the PV step).
   const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
+  const int vkey0 = 4 * (g16 >> 1) + jrow;
+  int voff[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db)
+    voff[db] = vkey0 * C::kVRow + vswz<D>(vkey0, db * 8 + (g16 & 1) * 4 + tcol) * 8;
 
   auto compute_tile = [&](int j, auto st) {
     const unsigned char* kl = k_of(st);
@@ -248,7 +270,7 @@ void attn_fwd_kernel(AttnArgs a) {
     const int k0 = j * kBN;
 
     // Each 32-key block of the tile is one online-softmax step.
-#pragma unroll 1
+#pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // ---- S^T = K Q^T for 32 keys x 32*RB rows ----
       f32x16 s[RB];
@@ -256,13 +278,11 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[rb][r] = 0.0f;
-      const int key = kb * 32 + l32;
-      const unsigned char* krow = &kl[key * C::kKRow];
+      const unsigned char* kblk = kl + kb * 32 * C::kKRow;
 #pragma unroll
       for (int kk = 0; kk < C::kQKSteps; ++kk) {
         if constexpr (!FP8) {
-          const int ck = (kk * 2 + hh) ^ (key & (C::kKSwz - 1));
-          const u32x4 kx = *(const u32x4*)(krow + ck * 16);
+          const u32x4 kx = *(const u32x4*)(kblk + koff[kk]);
           const bf16x8 af = __builtin_bit_cast(bf16x8, kx);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
@@ -270,10 +290,8 @@ void attn_fwd_kernel(AttnArgs a) {
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, qx), s[rb], 0, 0, 0);
           }
         } else {
-          const int ck0 = (kk * 4 + hh * 2) ^ (key & (C::kKSwz - 1));
-          const int ck1 = (kk * 4 + hh * 2 + 1) ^ (key & (C::kKSwz - 1));
-          const u32x4 k0x = *(const u32x4*)(krow + ck0 * 16);
-          const u32x4 k1x = *(const u32x4*)(krow + ck1 * 16);
+          const u32x4 k0x = *(const u32x4*)(kblk + koff[2 * kk]);
+          const u32x4 k1x = *(const u32x4*)(kblk + koff[2 * kk + 1]);
           const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
                             (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
 #pragma unroll
@@ -353,15 +371,13 @@ void attn_fwd_kernel(AttnArgs a) {
       // transposing 8-byte loads over keys base + 4 hh + (0..3) and base + 8 + 4 hh + (0..3).
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
-        const int chunk8 = db * 8 + (g16 & 1) * 4 + tcol;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int key_a = kb * 32 + 16 * e + 4 * (g16 >> 1) + jrow;
-          const int key_b = key_a + 8;
+          const unsigned char* va_p = vl + (kb * 32 + 16 * e) * C::kVRow + voff[db];
           const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(&vl[key_a * C::kVRow + vswz<D>(key_a, chunk8) * 8]));
+              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
           const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(&vl[key_b * C::kVRow + vswz<D>(key_b, chunk8) * 8]));
+              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
           const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
