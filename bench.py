@@ -33,10 +33,60 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--groups", type=int, default=1, help="head groups per rank (1 = single call, 5 = 2-head groups)")
+    ap.add_argument("--groups", type=int, default=5, help="head groups per rank (5 = 2-head groups, run one at a time; 1 = one call over all 10 heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows the oracle computes for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows the oracle computes for cpu_baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (HBM byte-counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "ulysses_sequence_attention_amd", "csrc", f)
+                  for f in ("attn.hip", "internal.h")]
+
+
+def kernel_source_hash() -> str:
+    """Hash of the attention kernel's sources and compile flags: counters taken
+    on another version of the kernel are not reported as its traffic."""
+    import hashlib
+    from ulysses_sequence_attention_amd import build as ubuild
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(ubuild.FLAGS).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(groups: int):
+    """HBM bytes per attention launch from the stored rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, each scaled by the same counter's reading for a plain copy
+    of known size; None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("per_groups", {}).get(str(groups))
+    if entry is None or t.get("source_sha256") != kernel_source_hash():
+        return None
+    return entry["hbm_bytes_per_launch"]
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, five times: reads 1 GiB and
+    writes 1 GiB per launch.  Run under `rocprofv3 --pmc FETCH_SIZE` (then
+    WRITE_SIZE) to get the counters' KiB per byte moved."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
 def cpu_baseline(q, k, v, rows_sample: int):
@@ -68,6 +118,9 @@ def cpu_baseline(q, k, v, rows_sample: int):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",
               file=sys.stderr)
@@ -165,7 +218,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fwd_kernel<128,false>",
+                     "traffic": measured_traffic(G), "kernel": "attn_fwd_kernel<128,false>",
                      "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
     }
     if not args.no_cpu_baseline:
