@@ -55,7 +55,7 @@ def kernel_source_hash() -> str:
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
-    h.update(" ".join(ubuild.FLAGS).encode())
+    h.update(" ".join(ubuild.FLAGS + ubuild.SOURCE_FLAGS.get("attn.hip", [])).encode())
     return h.hexdigest()
 
 

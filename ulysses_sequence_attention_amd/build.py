@@ -15,6 +15,9 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libulys.so")
 SOURCES = ["api.hip", "repack.hip", "attn.hip"]
+# per-source flags: the attention kernel interleaves MFMA and VALU work best
+# under the ILP-maximising machine scheduler
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 _EXTRA: list = []
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,7 +35,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *_EXTRA, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *_EXTRA, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

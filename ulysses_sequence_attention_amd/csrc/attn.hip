@@ -6,9 +6,8 @@
 // lse_i = ln sum_J exp(s_ij); kv head = h / (hq / hkv) (GQA).
 //
 // How (MI355X-first):
-//  * One workgroup = 256 query rows of one (b, h), split over the waves in
-//    32-row MFMA blocks (RB blocks per wave).  All waves share the K/V tiles
-//    in LDS.
+//  * One workgroup = 256 query rows of one (b, h): 8 waves of 32 rows, two
+//    waves per SIMD.  All waves share the K/V tiles in LDS.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (or the fp8 v_mfma_scale_f32_32x32x64_f8f6f4 for e4m3 q/k): in the
 //    accumulator every lane then holds ONE query row and 16 keys, so row max
@@ -24,6 +23,10 @@
 //  * 64-key tiles, double-buffered in LDS and filled by direct global->LDS
 //    16-byte loads (no staging registers): the next tile streams in while
 //    the current one is computed; one barrier per tile.
+//  * Within a tile the two 32-key blocks are software-pipelined: the QK^T
+//    MFMAs of block 1 are issued between the exp/convert instructions of
+//    block 0, and the PV MFMAs of block 0 between the row-max instructions of
+//    block 1, so each wave keeps its matrix core and vector ALU busy at once.
 //  * Online softmax in the exp2 domain per 32-key block with a lazy max: the
 //    running max is only raised (and O, l rescaled) when a block's max
 //    exceeds it by more than 2^8, a wave-uniform branch; probabilities stay
@@ -49,20 +52,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256;                     // query rows per workgroup
-constexpr int kBN = 64;                      // keys per LDS tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kWaves * 32;             // query rows per workgroup
+constexpr int kBN = 64;                      // keys per LDS tile (two 32-key blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
 
-#ifndef ULYS_ATTN_RB
-#define ULYS_ATTN_RB 1                       // 32-row MFMA blocks per wave
-#endif
-
-template <int D, bool FP8, int RB>
+template <int D, bool FP8>
 struct Cfg {
-  static constexpr int kWaves = kBM / (32 * RB);
-  static constexpr int kThreads = kWaves * 64;
   static constexpr int kQKBytes = FP8 ? 1 : 2;
   static constexpr int kKRow = D * kQKBytes;            // bytes per K row in LDS
   static constexpr int kKChunks = kKRow / 16;           // 16-byte chunks per K row
@@ -101,11 +100,12 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool FP8, int RB>
-__global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, FP8, RB>::kThreads, Cfg<D, FP8, RB>::kThreads),
-                          amdgpu_waves_per_eu(Cfg<D, FP8, RB>::kWaves / 4, Cfg<D, FP8, RB>::kWaves / 4)))
+#define ULYS_INLINE __attribute__((always_inline))
+
+template <int D, bool FP8>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
-  using C = Cfg<D, FP8, RB>;
+  using C = Cfg<D, FP8>;
   // One LDS array per stage, selected at compile time: the compiler can then
   // prove that the DMA filling one stage never aliases reads of the other and
   // does not wait for in-flight tile loads before every LDS read.
@@ -152,12 +152,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- Q fragments in registers (B operand of S^T = K Q^T) ----
   const size_t q_row_stride = (size_t)a.hq * D;            // elements
   const size_t kv_row_stride = (size_t)a.hkv * D;
-  const int qrow0 = qtile * kBM + wave * (32 * RB);
+  const int qrow0 = qtile * kBM + wave * 32;
   constexpr int kQRegs = FP8 ? 8 : 4;                       // dwords per fragment
-  unsigned int qf[RB][C::kQKSteps][kQRegs];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = qrow0 + rb * 32 + l32;
+  unsigned int qf[C::kQKSteps][kQRegs];
+  {
+    const int row = qrow0 + l32;
     const unsigned char* qp = (const unsigned char*)a.q +
         (((size_t)b * rows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
 #pragma unroll
@@ -167,8 +166,8 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int part = 0; part < kQRegs / 4; ++part) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (row < rows) x = ld16(qp + off + part * 16);
-        qf[rb][kk][part * 4 + 0] = x.x; qf[rb][kk][part * 4 + 1] = x.y;
-        qf[rb][kk][part * 4 + 2] = x.z; qf[rb][kk][part * 4 + 3] = x.w;
+        qf[kk][part * 4 + 0] = x.x; qf[kk][part * 4 + 1] = x.y;
+        qf[kk][part * 4 + 2] = x.z; qf[kk][part * 4 + 3] = x.w;
       }
     }
   }
@@ -187,8 +186,8 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int kKRowsPerSeg = 1024 / C::kKRow;
 #pragma unroll
     for (int u = 0; u < C::kKSegsPerWave; ++u) {
-      const int seg = wave + u * C::kWaves;
-      if (C::kKSegs % C::kWaves != 0 && seg >= C::kKSegs) break;   // wave-uniform
+      const int seg = wave + u * kWaves;
+      if (C::kKSegs % kWaves != 0 && seg >= C::kKSegs) break;   // wave-uniform
       const int key = seg * kKRowsPerSeg + lane / C::kKChunks;
       const int sck = lane % C::kKChunks;
       const int ck = sck ^ (key & (C::kKSwz - 1));
@@ -200,8 +199,8 @@ void attn_fwd_kernel(AttnArgs a) {
     constexpr int kVRowsPerSeg = 1024 / C::kVRow;
 #pragma unroll
     for (int u = 0; u < C::kVSegsPerWave; ++u) {
-      const int seg = wave + u * C::kWaves;
-      if (C::kVSegs % C::kWaves != 0 && seg >= C::kVSegs) break;   // wave-uniform
+      const int seg = wave + u * kWaves;
+      if (C::kVSegs % kWaves != 0 && seg >= C::kVSegs) break;   // wave-uniform
       const int key = seg * kVRowsPerSeg + lane / C::kVChunks;
       const int sck = lane % C::kVChunks;                 // 16-byte slot in the LDS row
       const int ck = vswz<D>(key, 2 * sck) >> 1;          // its global 16-byte chunk
@@ -213,17 +212,13 @@ void attn_fwd_kernel(AttnArgs a) {
   };
 
   // ---- running state ----
-  f32x16 o[RB][C::kDB];
+  f32x16 o[C::kDB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.0f;
-  float m_run[RB];          // running max of c*log2e*s (lazy)
-  float l_run[RB][2];       // partial row sums (two chains)
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb][0] = 0.0f; l_run[rb][1] = 0.0f; }
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m_run = -INFINITY;              // running max of c*log2e*s (lazy)
+  float l_run0 = 0.0f, l_run1 = 0.0f;   // partial row sums (two chains)
 
   // End of a tile: this wave's tile loads have landed and its LDS reads are
   // done (s_waitcnt vmcnt(0) lgkmcnt(0), as a builtin so the compiler's own
@@ -256,7 +251,7 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   }
   //  V (A operand of O^T, transposing reads): within 16 lanes, lane 4j+t reads
-  //  row key0 + j at head-dim d0 + 4t.. (see the PV step).
+  //  row key0 + j at head-dim d0 + 4t.. (see pv).
   const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
   const int vkey0 = 4 * (g16 >> 1) + jrow;
   int voff[C::kDB];
@@ -264,128 +259,137 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int db = 0; db < C::kDB; ++db)
     voff[db] = vkey0 * C::kVRow + vswz<D>(vkey0, db * 8 + (g16 & 1) * 4 + tcol) * 8;
 
+  // ---- block pieces ----
+  // S^T for the 32 keys kb*32.. of the tile in K stage `kl`.
+  auto qk = [&](const unsigned char* kl, int kb) ULYS_INLINE {
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    const unsigned char* kblk = kl + kb * 32 * C::kKRow;
+#pragma unroll
+    for (int kk = 0; kk < C::kQKSteps; ++kk) {
+      if constexpr (!FP8) {
+        const u32x4 kx = *(const u32x4*)(kblk + koff[kk]);
+        const u32x4 qx = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), __builtin_bit_cast(bf16x8, qx), s,
+                                                    0, 0, 0);
+      } else {
+        const u32x4 k0x = *(const u32x4*)(kblk + koff[2 * kk]);
+        const u32x4 k1x = *(const u32x4*)(kblk + koff[2 * kk + 1]);
+        const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
+                          (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
+        const i32x8 bq = {(int)qf[kk][0], (int)qf[kk][1], (int)qf[kk][2], (int)qf[kk][3],
+                          (int)qf[kk][4], (int)qf[kk][5], (int)qf[kk][6], (int)qf[kk][7]};
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s, 0, 0, 0, 127, 0, 127);
+      }
+    }
+    return s;
+  };
+
+  // Tail keys and keys inside the gap -> -inf: branch-free selects under one
+  // wave-uniform branch (the key of register r is kb0 + 8 (r/4) + 4 hh + r%4).
+  auto mask = [&](f32x16& s, int kb0) ULYS_INLINE {
+    if (kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs)) {
+      const int kl = kb0 + 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kidx = kl + 8 * (r >> 2) + (r & 3);
+        const bool dead = (kidx >= rows) | ((kidx >= gs) & (kidx < ge));
+        s[r] = dead ? -INFINITY : s[r];
+      }
+    }
+  };
+
+  // Row max of a block, in the exp2 domain.
+  auto rowmax = [&](const f32x16& s) ULYS_INLINE {
+    float m = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+    return lane_swap_max(m) * c2;
+  };
+
+  // Lazy rescale before a block's probabilities are formed.
+  auto rescale = [&](float mx) ULYS_INLINE {
+    if (__any(mx > m_run + kLazy)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run0 *= alpha;
+      l_run1 *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+  };
+
+  // Probabilities -> bf16 B operands of the PV MFMA (p[e] = accumulator
+  // registers 8e..8e+7) and fp32 row sums.
+  auto probs = [&](const f32x16& s, bf16x8 (&p)[2]) ULYS_INLINE {
+    const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, -mb));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, -mb));
+        const f32x2 xx = {x0, x1};
+        const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
+        p[e][2 * i] = pk[0];
+        p[e][2 * i + 1] = pk[1];
+        l_run0 += x0;
+        l_run1 += x1;
+      }
+  };
+
+  // The probabilities and row sums are complete here (the empty asm consumes
+  // them), so the compiler schedules their VALU work between the QK^T MFMAs
+  // issued before this point instead of sinking it past the mask branch.
+  auto pin = [&](const bf16x8 (&pp)[2]) ULYS_INLINE {
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pp[0])), "v"(__builtin_bit_cast(u32x4, pp[1])), "v"(l_run0),
+                 "v"(l_run1));
+  };
+
+  // O^T += V^T P^T for the 32 keys kb*32.. of the tile in V stage `vl`.  A
+  // operand of lane l: V[key(hh, i)][d = 32 db + l%32], i = 0..7, read as two
+  // transposing 8-byte loads over keys base + 4 hh + (0..3) and
+  // base + 8 + 4 hh + (0..3) -- the keys whose probabilities p[e] holds.
+  auto pv = [&](const unsigned char* vl, int kb, const bf16x8 (&p)[2]) ULYS_INLINE {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const unsigned char* va_p = vl + (kb * 32 + 16 * e) * C::kVRow + voff[db];
+        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
+        const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
+        const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[e], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // One tile, software-pipelined over its two blocks:
+  //   QK 0, mask/max/rescale 0 | {QK 1 + probabilities 0} | mask 1 |
+  //   {PV 0 + row max 1} | rescale 1, probabilities 1, PV 1.
   auto compute_tile = [&](int j, auto st) {
     const unsigned char* kl = k_of(st);
     const unsigned char* vl = v_of(st);
     const int k0 = j * kBN;
-
-    // Each 32-key block of the tile is one online-softmax step.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T for 32 keys x 32*RB rows ----
-      f32x16 s[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[rb][r] = 0.0f;
-      const unsigned char* kblk = kl + kb * 32 * C::kKRow;
-#pragma unroll
-      for (int kk = 0; kk < C::kQKSteps; ++kk) {
-        if constexpr (!FP8) {
-          const u32x4 kx = *(const u32x4*)(kblk + koff[kk]);
-          const bf16x8 af = __builtin_bit_cast(bf16x8, kx);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const u32x4 qx = {qf[rb][kk][0], qf[rb][kk][1], qf[rb][kk][2], qf[rb][kk][3]};
-            s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, qx), s[rb], 0, 0, 0);
-          }
-        } else {
-          const u32x4 k0x = *(const u32x4*)(kblk + koff[2 * kk]);
-          const u32x4 k1x = *(const u32x4*)(kblk + koff[2 * kk + 1]);
-          const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
-                            (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const i32x8 bq = {(int)qf[rb][kk][0], (int)qf[rb][kk][1], (int)qf[rb][kk][2], (int)qf[rb][kk][3],
-                              (int)qf[rb][kk][4], (int)qf[rb][kk][5], (int)qf[rb][kk][6], (int)qf[rb][kk][7]};
-            s[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s[rb], 0, 0, 0, 127, 0, 127);
-          }
-        }
-      }
-
-      // ---- mask: tail keys and keys inside the gap ----
-      // Branch-free selects per register (the key of register r is
-      // kb0 + 8 (r / 4) + 4 hh + r % 4), under one wave-uniform branch.
-      const int kb0 = k0 + kb * 32;
-      if (kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs)) {
-        const int kl = kb0 + 4 * hh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = kl + 8 * (r >> 2) + (r & 3);
-          const bool dead = (kidx >= rows) | ((kidx >= gs) & (kidx < ge));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][r] = dead ? -INFINITY : s[rb][r];
-        }
-      }
-
-      // ---- online softmax (exp2 domain, lazy max) ----
-      float mx[RB];
-      bool need = false;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float m = s[rb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, s[rb][r]);
-        m = lane_swap_max(m);
-        mx[rb] = m * c2;
-        need = need || (mx[rb] > m_run[rb] + kLazy);
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mn = fmaxf(m_run[rb], mx[rb]);
-          const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
-          m_run[rb] = mn;
-          l_run[rb][0] *= alpha;
-          l_run[rb][1] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
-        }
-      }
-
-      // probabilities -> bf16 B operands of the PV MFMA: p[rb][e] holds
-      // accumulator registers 8e..8e+7 of s[rb]
-      bf16x8 p[RB][2];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mb = (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * e + 2 * i], c2, -mb));
-            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * e + 2 * i + 1], c2, -mb));
-            const f32x2 xx = {x0, x1};
-            const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
-            p[rb][e][2 * i] = pk[0];
-            p[rb][e][2 * i + 1] = pk[1];
-            l_run[rb][0] += x0;
-            l_run[rb][1] += x1;
-          }
-      }
-
-      // ---- O^T += V^T P^T ----
-      // A operand of lane l: V[key(hh, i)][d = 32 db + l%32], i = 0..7, read as two
-      // transposing 8-byte loads over keys base + 4 hh + (0..3) and base + 8 + 4 hh + (0..3).
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const unsigned char* va_p = vl + (kb * 32 + 16 * e) * C::kVRow + voff[db];
-          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
-          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
-          const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[rb][e], o[rb][db], 0, 0, 0);
-        }
-      }
-    }
-
+    bf16x8 p[2];
+    f32x16 s0 = qk(kl, 0);
+    mask(s0, k0);
+    rescale(rowmax(s0));
+    f32x16 s1 = qk(kl, 1);
+    probs(s0, p);
+    pin(p);
+    mask(s1, k0 + 32);
+    pv(vl, 0, p);
+    const float m1 = rowmax(s1);
+    rescale(m1);
+    probs(s1, p);
+    pv(vl, 1, p);
   };
 
   // Tiles alternate between the two stages; the next tile's loads are issued
@@ -406,10 +410,9 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = qrow0 + rb * 32 + l32;
-    const float l = lane_swap_sum(l_run[rb][0] + l_run[rb][1]);
+  {
+    const int row = qrow0 + l32;
+    const float l = lane_swap_sum(l_run0 + l_run1);
     const float inv = 1.0f / l;
     if (row < rows) {
       uint16_t* op = a.o + ((size_t)b * rows + row) * q_row_stride + (size_t)head * D;
@@ -417,8 +420,8 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x2 lo = {o[rb][db][4 * r4 + 0] * inv, o[rb][db][4 * r4 + 1] * inv};
-          const f32x2 hi = {o[rb][db][4 * r4 + 2] * inv, o[rb][db][4 * r4 + 3] * inv};
+          const f32x2 lo = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv};
+          const f32x2 hi = {o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
           const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
           const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
           u32x2 w;
@@ -427,16 +430,15 @@ void attn_fwd_kernel(AttnArgs a) {
           *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
         }
       if (a.lse != nullptr && hh == 0)
-        a.lse[((size_t)b * a.hq + head) * rows + row] = (m_run[rb] + __log2f(l)) * kLn2;
+        a.lse[((size_t)b * a.hq + head) * rows + row] = (m_run + __log2f(l)) * kLn2;
     }
   }
 }
 
 template <int D, bool FP8>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  using C = Cfg<D, FP8, ULYS_ATTN_RB>;
   dim3 grid((a.rows + kBM - 1) / kBM, a.hq, a.batch);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, ULYS_ATTN_RB>), grid, dim3(C::kThreads), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
