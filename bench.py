@@ -74,6 +74,25 @@ def measured_traffic(groups: int):
     return entry["hbm_bytes_per_launch"]
 
 
+def device_copy_gbs(torch) -> float:
+    """Practical HBM ceiling for a stream: a plain 1 GiB device-to-device copy
+    (torch copy_), read + write bytes over the median of 5 timed copies."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del src, dst
+    return 2 * n / (sorted(times)[2] * 1e-3) / 1e9
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB, five times: reads 1 GiB and
     writes 1 GiB per launch.  Run under `rocprofv3 --pmc FETCH_SIZE` (then
@@ -221,6 +240,7 @@ def main():
                      "traffic": measured_traffic(G), "kernel": "attn_fwd_kernel<128,false>",
                      "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
     }
+    res["hbm_copy_gbs"] = round(device_copy_gbs(torch), 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_rows)
     print(json.dumps(res))
