@@ -10,8 +10,10 @@ repack does not re-read one rank's bytes from cache.
 `value` = attention TFLOP/s of the whole step (4*N^2*D*heads per step over
 the step time, pack and unpack included).  The JSON line also carries the
 attention kernel's own rate (`roofline`, HIP events around each launch on the
-launch stream), the repack GB/s, and the CPU oracle timed on a bounded
-sample (`cpu_baseline`).
+launch stream), the repack GB/s, the same steps under the two-stream group
+pipeline (ulys_rank_pipeline; `--pipeline` times that one instead), a plain
+device copy rate, and the CPU oracle timed on a bounded sample
+(`cpu_baseline`).
 """
 from __future__ import annotations
 
@@ -34,6 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--groups", type=int, default=5, help="head groups per rank (5 = 2-head groups, run one at a time; 1 = one call over all 10 heads)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time ulys_rank_pipeline (per-group repack on a second stream overlapping attention) "
+                         "instead of the one-stream step (pack all groups, attend each, unpack all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows the oracle computes for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,6 +170,7 @@ def main():
     lse = torch.empty((G, 1, gh, rows), dtype=torch.float32, device=dev)
     out = [torch.empty_like(s) for s in shards["q"]]
     stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
 
     flops_step = 4.0 * rows * rows * D * (H // P)
     bytes_pack = 2 * 3 * rows * (H // P) * D * 2       # read + write, q/k/v bf16
@@ -172,7 +178,12 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(rank, rec=None):
+    def step(rank, pipelined, rec=None):
+        if pipelined:
+            # the pages' per-group pipeline: pack(g+2)/unpack(g) on the copy stream overlap attention(g)
+            ulys.ulys_rank_pipeline(L, rank, shards["q"], shards["k"], shards["v"], qs, ks, vs, os_, out, lse=lse,
+                                    stream=stream, copy_stream=copy_stream)
+            return
         if rec is not None:
             rec["p0"].record(stream)
         ulys.ulys_pack(L, rank, -1, shards["q"], shards["k"], shards["v"], qs, ks, vs)
@@ -186,20 +197,29 @@ def main():
         if rec is not None:
             rec["u1"].record(stream)
 
-    for i in range(args.warmup):
-        step(i % P)
-    torch.cuda.synchronize()
+    def timed(pipelined):
+        """Warm-up, then exactly `steps` steps between two events; per-kernel events in sequential mode."""
+        for i in range(args.warmup):
+            step(i % P, pipelined)
+        torch.cuda.synchronize()
+        recs = None if pipelined else [{k_: ev() for k_ in ("p0", "p1", "a1", "u1")} for _ in range(args.steps)]
+        t0, t1 = ev(), ev()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i % P, pipelined, None if recs is None else recs[i])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps, recs
 
-    recs = [{k_: ev() for k_ in ("p0", "p1", "a1", "u1")} for _ in range(args.steps)]
-    t0, t1 = ev(), ev()
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i % P, recs[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
+    pipelined = args.pipeline
+    ms_step, recs = timed(pipelined)
+    if pipelined:
+        # per-kernel rates: the same steps again on one stream, events around each kernel group
+        other_ms_step, recs = timed(False)
+    else:
+        # the two-stream schedule of the same steps, for comparison
+        other_ms_step, _ = timed(True)
     pack_ms = sum(r["p0"].elapsed_time(r["p1"]) for r in recs) / args.steps
     attn_ms = sum(r["p1"].elapsed_time(r["a1"]) for r in recs) / args.steps
     unpack_ms = sum(r["a1"].elapsed_time(r["u1"]) for r in recs) / args.steps
@@ -224,7 +244,9 @@ def main():
         "config": {"workload": f"Wan2.1 Ulysses-4 share: 4 shards [1,6820,40,128] -> pack 10 heads into {G} "
                                f"slot(s) [1,27280,{gh},128] -> attention N=27280 D=128 non-causal + LSE -> unpack",
                    "batch": 1, "seq_len": rows, "heads_per_gpu": H // P, "head_dim": D, "head_groups": G,
-                   "ulysses_degree_simulated": P},
+                   "ulysses_degree_simulated": P,
+                   "schedule": "two-stream group pipeline" if pipelined else "one stream, sequential"},
+        ("sequential_ms_per_step" if pipelined else "pipelined_ms_per_step"): round(other_ms_step, 4),
         "attention_tflops": round(attn_tflops, 2),
         "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "attention_ms": round(attn_ms, 4),

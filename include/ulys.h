@@ -6,8 +6,9 @@
  *   ulys_pack          shards -> per-head-group receive slots (+ optional e4m3 q/k)
  *   ulys_attend_group  dense non-causal attention + log-sum-exp on one slot
  *   ulys_unpack        output slot -> output shards
- * plus ulys_amax_bf16 (per-tensor fp8 scale source), ulys_strerror and
- * ulys_last_error.
+ * plus ulys_rank_pipeline (the three steps for every head group of a rank,
+ * repack overlapping attention on a second stream), ulys_amax_bf16
+ * (per-tensor fp8 scale source), ulys_strerror and ulys_last_error.
  *
  * Conventions shared by every call
  *   - Tensors are caller-owned device memory, dense, row-major, with the
@@ -16,7 +17,8 @@
  *   - Arrays of pointers and key gaps are host memory, read only during the
  *     call; the caller may reuse them on return.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
- *     work on it; none synchronises, allocates, or keeps state between calls.
+ *     work on it; none synchronises, allocates device memory, or keeps state
+ *     between calls.
  *   - All validation happens before anything is enqueued.  On failure the
  *     call returns a negative ulys_status, enqueues nothing, and
  *     ulys_last_error() describes the first violated rule.
@@ -175,6 +177,43 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  */
 int ulys_unpack(const ulys_layout* layout, int rank, int group,
                 const void* o_slot, void* const* o_shards, void* stream);
+
+/*
+ * ulys_rank_pipeline -- one rank's whole path, head group by head group, with
+ * the repack of neighbouring groups overlapping each group's attention.
+ *
+ * Source: sglang PR #43521, "Motivation" and "Receive slots" (split the
+ * heads into groups and run exchange-in(g+1) and exchange-out(g-1) on a
+ * second stream while group g attends, each group in its own receive slot,
+ * with events between the streams; the result must be the sequential
+ * exchange's, bit for bit) and "Host cost" (no host synchronisation inside
+ * the loop).
+ *
+ * Equivalent to, for g = 0 .. G-1 in order:
+ *   ulys_pack(layout, rank, g, ...) into slot g,
+ *   ulys_attend_group(B, rows, Gq, Gkv, D, slot g ..., o slot g, lse g),
+ *   ulys_unpack(layout, rank, g, o slot g, o_shards)
+ * and byte-identical to it.  q/k/v/o_slots hold G consecutive slots
+ * ([G][B, rows, Gh, D], the group = -1 layout of ulys_pack); lse is
+ * [G][B, Gq, rows] float32 or NULL.  Shards, qk_dtype, qk_amax,
+ * softmax_scale and key_gaps as for ulys_pack / ulys_attend_group.
+ *
+ * Streams: attention runs on `stream`, packs and unpacks on `copy_stream`
+ * (pack(g+2) and unpack(g) follow attention g there).  The call orders the
+ * copy stream after work already enqueued on `stream`, and work enqueued on
+ * `stream` after the call after the last unpack, so the caller synchronises
+ * on `stream` alone.  Passing the same stream twice runs everything in order
+ * on it.  Every rule of the three calls is checked before anything is
+ * enqueued; G <= 64 (ULYS_EUNSUPPORTED otherwise).  The call creates 2G + 2
+ * HIP events and releases them before returning (ULYS_EHIP if creation fails).
+ */
+int ulys_rank_pipeline(const ulys_layout* layout, int rank,
+                       const void* const* q_shards, const void* const* k_shards,
+                       const void* const* v_shards,
+                       void* q_slots, void* k_slots, void* v_slots, void* o_slots,
+                       float* lse, void* const* o_shards,
+                       int qk_dtype, const float* qk_amax, float softmax_scale,
+                       const int32_t* key_gaps, void* stream, void* copy_stream);
 
 /* Static text for a ulys_status value. */
 const char* ulys_strerror(int status);

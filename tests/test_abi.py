@@ -28,7 +28,8 @@ def _declared():
 
 def test_header_declares_the_path():
     names = _declared()
-    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
+    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_amax_bf16",
+              "ulys_strerror", "ulys_last_error"):
         assert n in names
 
 
@@ -132,6 +133,31 @@ def test_unpack_and_amax_rules(U):
     assert U.call_raw("ulys_amax_bf16", _arr(1), 1, 12, FAKE, None) == -1
     assert U.call_raw("ulys_amax_bf16", _arr(1), 1, 8, None, None) == -1
     assert U.call_raw("ulys_amax_bf16", _arr(1, MIS), 1, 8, FAKE, None) == -1
+
+
+def _pipeline(U, L, rank=0, slots=(FAKE,) * 4, lse=None, out=None, dtype=0, amax=FAKE, scale=0.0, gaps=None):
+    c = U.Layout(**L).c_struct()
+    P = c.degree
+    out = _arr(P) if out is None else out
+    g = None if gaps is None else (ctypes.c_int32 * len(gaps))(*gaps)
+    return U.call_raw("ulys_rank_pipeline", ctypes.byref(c), rank, _arr(P), _arr(P), _arr(P), *slots, lse, out,
+                      dtype, amax, ctypes.c_float(scale), g, None, None)
+
+
+def test_pipeline_rules(U):
+    """Every rule of pack, attend and unpack is checked before anything is enqueued."""
+    assert _pipeline(U, dict(GOOD, hq=42)) == -1                       # layout
+    assert _pipeline(U, GOOD, rank=4) == -1
+    assert _pipeline(U, GOOD, slots=(FAKE, None, FAKE, FAKE)) == -1    # k slots
+    assert _pipeline(U, GOOD, slots=(FAKE, FAKE, FAKE, MIS)) == -1     # o slots misaligned
+    assert _pipeline(U, GOOD, out=_arr(4, MIS)) == -1                  # output shards
+    assert _pipeline(U, GOOD, lse=FAKE + 2) == -1
+    assert _pipeline(U, GOOD, dtype=1, amax=None) == -1                # fp8 without amax
+    assert _pipeline(U, GOOD, scale=float("nan")) == -1
+    assert _pipeline(U, GOOD, gaps=[0, 40]) == -1                      # no valid key (40 joint rows)
+    assert "no valid key" in U.last_error()
+    assert _pipeline(U, dict(GOOD, head_dim=96)) == -2
+    assert _pipeline(U, dict(GOOD, hq=4 * 65, hkv=4 * 65, groups=65)) == -2   # more than 64 groups
 
 
 def test_strerror(U):

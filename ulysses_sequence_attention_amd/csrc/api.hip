@@ -93,9 +93,14 @@ int hip_status(hipError_t e) {
 
 extern "C" {
 
-int ulys_pack(const ulys_layout* L, int rank, int group, const void* const* q_shards,
-              const void* const* k_shards, const void* const* v_shards, void* q_slot, void* k_slot,
-              void* v_slot, int qk_dtype, const float* qk_amax, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validated launch arguments of a pack; nothing is enqueued.
+int prepare_pack(const ulys_layout* L, int rank, int group, const void* const* q_shards,
+                 const void* const* k_shards, const void* const* v_shards, void* q_slot, void* k_slot,
+                 void* v_slot, int qk_dtype, const float* qk_amax, ulys::PackArgs& a) {
   int st = check_layout(L, rank, group);
   if (st) return st;
   if (qk_dtype != ULYS_BF16 && qk_dtype != ULYS_FP8_E4M3) return fail(ULYS_EINVAL, "qk_dtype %d unknown", qk_dtype);
@@ -109,7 +114,6 @@ int ulys_pack(const ulys_layout* L, int rank, int group, const void* const* q_sh
   if (fp8 && qk_amax == nullptr) return fail(ULYS_EINVAL, "qk_amax is NULL with fp8 q/k");
   if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
 
-  ulys::PackArgs a;
   memset(&a, 0, sizeof a);
   a.g = geom_of(L, rank, group);
   const int heads[3] = {L->hq, L->hkv, L->hkv};
@@ -125,29 +129,13 @@ int ulys_pack(const ulys_layout* L, int rank, int group, const void* const* q_sh
     a.fp8[t] = (fp8 && t < 2) ? 1 : 0;
   }
   a.amax = qk_amax;
-  return hip_status(ulys::launch_pack(a, (hipStream_t)stream));
+  return ULYS_OK;
 }
 
-int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each, float* amax_out, void* stream) {
-  if (n_tensors < 1 || n_tensors > ulys::kMaxAmaxTensors)
-    return fail(ULYS_EINVAL, "n_tensors %d outside [1, %d]", n_tensors, ulys::kMaxAmaxTensors);
-  int st = check_ptr_array(tensors, n_tensors, "tensors");
-  if (st) return st;
-  if (elems_each % 8) return fail(ULYS_EINVAL, "elems_each %zu is not a multiple of 8", elems_each);
-  if (amax_out == nullptr) return fail(ULYS_EINVAL, "amax_out is NULL");
-  if ((uintptr_t)amax_out & 3u) return fail(ULYS_EINVAL, "amax_out is not 4-byte aligned");
-  ulys::AmaxArgs a;
-  memset(&a, 0, sizeof a);
-  for (int i = 0; i < n_tensors; ++i) a.src[i] = (const uint16_t*)tensors[i];
-  a.n = n_tensors;
-  a.chunks_each = elems_each / 8;
-  a.out = (unsigned int*)amax_out;
-  return hip_status(ulys::launch_amax(a, (hipStream_t)stream));
-}
-
-int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
-                      const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
-                      const int32_t* key_gaps, void* o, float* lse, void* stream) {
+// Validated launch arguments of an attention call; nothing is enqueued.
+int prepare_attend(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
+                   const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
+                   const int32_t* key_gaps, void* o, float* lse, ulys::AttnArgs& a) {
   if (batch < 1 || rows < 1 || hq < 1 || hkv < 1)
     return fail(ULYS_EINVAL, "batch, rows, hq and hkv must be >= 1");
   if (hq % hkv) return fail(ULYS_EINVAL, "hq %d must be a multiple of hkv %d", hq, hkv);
@@ -167,7 +155,6 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const 
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(ULYS_EINVAL, "softmax_scale must be finite");
 
-  ulys::AttnArgs a;
   memset(&a, 0, sizeof a);
   if (key_gaps != nullptr) {
     if (batch > ulys::kMaxGapBatch) return fail(ULYS_EINVAL, "key gaps for batch %d > %d", batch, ulys::kMaxGapBatch);
@@ -192,15 +179,16 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const 
   a.rows = rows;
   a.hq = hq;
   a.hkv = hkv;
-  return hip_status(ulys::launch_attn(a, head_dim, fp8, (hipStream_t)stream));
+  return ULYS_OK;
 }
 
-int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, void* const* o_shards, void* stream) {
+// Validated launch arguments of an unpack; nothing is enqueued.
+int prepare_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, void* const* o_shards,
+                   ulys::UnpackArgs& a) {
   int st = check_layout(L, rank, group);
   if (st) return st;
   if ((st = check_ptr(o_slot, "o_slot"))) return st;
   if ((st = check_ptr_array((const void* const*)o_shards, L->degree, "o_shards"))) return st;
-  ulys::UnpackArgs a;
   memset(&a, 0, sizeof a);
   a.g = geom_of(L, rank, group);
   a.src = (const uint16_t*)o_slot;
@@ -208,7 +196,150 @@ int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, v
   a.heads = L->hq;
   a.gh = L->hq / L->degree / L->groups;
   a.h0 = rank * (L->hq / L->degree) + (group < 0 ? 0 : group) * a.gh;
+  return ULYS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ulys_pack(const ulys_layout* L, int rank, int group, const void* const* q_shards,
+              const void* const* k_shards, const void* const* v_shards, void* q_slot, void* k_slot,
+              void* v_slot, int qk_dtype, const float* qk_amax, void* stream) {
+  ulys::PackArgs a;
+  const int st = prepare_pack(L, rank, group, q_shards, k_shards, v_shards, q_slot, k_slot, v_slot, qk_dtype,
+                              qk_amax, a);
+  if (st) return st;
+  return hip_status(ulys::launch_pack(a, (hipStream_t)stream));
+}
+
+int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each, float* amax_out, void* stream) {
+  if (n_tensors < 1 || n_tensors > ulys::kMaxAmaxTensors)
+    return fail(ULYS_EINVAL, "n_tensors %d outside [1, %d]", n_tensors, ulys::kMaxAmaxTensors);
+  int st = check_ptr_array(tensors, n_tensors, "tensors");
+  if (st) return st;
+  if (elems_each % 8) return fail(ULYS_EINVAL, "elems_each %zu is not a multiple of 8", elems_each);
+  if (amax_out == nullptr) return fail(ULYS_EINVAL, "amax_out is NULL");
+  if ((uintptr_t)amax_out & 3u) return fail(ULYS_EINVAL, "amax_out is not 4-byte aligned");
+  ulys::AmaxArgs a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < n_tensors; ++i) a.src[i] = (const uint16_t*)tensors[i];
+  a.n = n_tensors;
+  a.chunks_each = elems_each / 8;
+  a.out = (unsigned int*)amax_out;
+  return hip_status(ulys::launch_amax(a, (hipStream_t)stream));
+}
+
+int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
+                      const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
+                      const int32_t* key_gaps, void* o, float* lse, void* stream) {
+  ulys::AttnArgs a;
+  const int st = prepare_attend(batch, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax, key_gaps,
+                                o, lse, a);
+  if (st) return st;
+  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
+}
+
+int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, void* const* o_shards, void* stream) {
+  ulys::UnpackArgs a;
+  const int st = prepare_unpack(L, rank, group, o_slot, o_shards, a);
+  if (st) return st;
   return hip_status(ulys::launch_unpack(a, (hipStream_t)stream));
+}
+
+int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shards, const void* const* k_shards,
+                       const void* const* v_shards, void* q_slots, void* k_slots, void* v_slots, void* o_slots,
+                       float* lse, void* const* o_shards, int qk_dtype, const float* qk_amax, float softmax_scale,
+                       const int32_t* key_gaps, void* stream, void* copy_stream) {
+  // Validate everything with group -1 (all groups) before anything is enqueued.
+  ulys::PackArgs pk;
+  int st = prepare_pack(L, rank, -1, q_shards, k_shards, v_shards, q_slots, k_slots, v_slots, qk_dtype, qk_amax, pk);
+  if (st) return st;
+  ulys::UnpackArgs up;
+  if ((st = prepare_unpack(L, rank, -1, o_slots, o_shards, up))) return st;
+  const int G = L->groups;
+  const int rows = pk.g.rows;
+  const int gq = L->hq / L->degree / G, gkv = L->hkv / L->degree / G;
+  ulys::AttnArgs at;
+  if ((st = prepare_attend(L->batch, rows, gq, gkv, L->head_dim, q_slots, k_slots, v_slots, qk_dtype, softmax_scale,
+                           qk_amax, key_gaps, o_slots, lse, at)))
+    return st;
+  if (G > ulys::kMaxPipelineGroups)
+    return fail(ULYS_EUNSUPPORTED, "pipeline of %d groups exceeds %d", G, ulys::kMaxPipelineGroups);
+  const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
+  const size_t qk_elem = fp8 ? 1 : 2;
+  const size_t elems_q = (size_t)L->batch * rows * gq * L->head_dim;
+  const size_t elems_kv = (size_t)L->batch * rows * gkv * L->head_dim;
+  hipStream_t cs = (hipStream_t)stream, xs = (hipStream_t)copy_stream;
+
+  // Events: start (compute -> copy), pack(g) (copy -> compute), attend(g)
+  // (compute -> copy), done (copy -> compute).  Destroying a recorded event
+  // before it completes is deferred by the runtime, so they are released at
+  // the end of the call.
+  hipEvent_t ev[2 * ulys::kMaxPipelineGroups + 2];
+  const int nev = 2 * G + 2;
+  for (int i = 0; i < nev; ++i) {
+    const hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return hip_status(e);
+    }
+  }
+  hipEvent_t ev_start = ev[0], ev_done = ev[1];
+  hipEvent_t* ev_pack = ev + 2;
+  hipEvent_t* ev_att = ev + 2 + G;
+
+  auto pack_g = [&](int g) {
+    ulys::PackArgs a = pk;
+    a.g.ngroups = 1;
+    for (int t = 0; t < 3; ++t) {
+      const size_t bytes = (t == 0 ? elems_q : elems_kv) * (t < 2 ? qk_elem : 2);
+      a.dst[t] = (unsigned char*)pk.dst[t] + (size_t)g * bytes;
+      a.h0[t] = pk.h0[t] + g * pk.gh[t];
+    }
+    return ulys::launch_pack(a, xs);
+  };
+  auto attend_g = [&](int g) {
+    ulys::AttnArgs a = at;
+    a.q = (const unsigned char*)q_slots + (size_t)g * elems_q * qk_elem;
+    a.k = (const unsigned char*)k_slots + (size_t)g * elems_kv * qk_elem;
+    a.v = (const unsigned char*)v_slots + (size_t)g * elems_kv * 2;
+    a.o = (uint16_t*)o_slots + (size_t)g * elems_q;
+    a.lse = lse == nullptr ? nullptr : lse + (size_t)g * L->batch * gq * rows;
+    return ulys::launch_attn(a, L->head_dim, fp8, cs);
+  };
+  auto unpack_g = [&](int g) {
+    ulys::UnpackArgs a = up;
+    a.g.ngroups = 1;
+    a.src = (const uint16_t*)o_slots + (size_t)g * elems_q;
+    a.h0 = up.h0 + g * up.gh;
+    return ulys::launch_unpack(a, xs);
+  };
+
+  // copy stream: pack 0, pack 1, [attend 0] unpack 0, pack 2, [attend 1] unpack 1, ...
+  // compute stream: [pack g] attend g.  Each group has its own slots, so a
+  // pack only has to precede its own attention and an unpack follow it.
+  hipError_t e = hipEventRecord(ev_start, cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_start, 0);
+  for (int g = 0; e == hipSuccess && g < G && g < 2; ++g) {
+    e = pack_g(g);
+    if (e == hipSuccess) e = hipEventRecord(ev_pack[g], xs);
+  }
+  for (int g = 0; e == hipSuccess && g < G; ++g) {
+    e = hipStreamWaitEvent(cs, ev_pack[g], 0);
+    if (e == hipSuccess) e = attend_g(g);
+    if (e == hipSuccess) e = hipEventRecord(ev_att[g], cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_att[g], 0);
+    if (e == hipSuccess) e = unpack_g(g);
+    if (e == hipSuccess && g + 2 < G) {
+      e = pack_g(g + 2);
+      if (e == hipSuccess) e = hipEventRecord(ev_pack[g + 2], xs);
+    }
+  }
+  if (e == hipSuccess) e = hipEventRecord(ev_done, xs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev_done, 0);
+  for (int i = 0; i < nev; ++i) (void)hipEventDestroy(ev[i]);
+  return hip_status(e);
 }
 
 const char* ulys_strerror(int status) {

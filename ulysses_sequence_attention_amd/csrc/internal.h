@@ -9,6 +9,7 @@ namespace ulys {
 
 constexpr int kMaxDegree = 64;      // P shards per call (kernel-argument arrays)
 constexpr int kMaxGapBatch = 256;   // batches that may carry a key gap
+constexpr int kMaxPipelineGroups = 64;   // head groups of one ulys_rank_pipeline call
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.

@@ -46,12 +46,17 @@ _lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes
 _lib.ulys_attend_group.restype = _i
 _lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.POINTER(_vp), _vp]
 _lib.ulys_unpack.restype = _i
+_lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _i, _vp,
+                                    ctypes.c_float, _vp, _vp, _vp]
+_lib.ulys_rank_pipeline.restype = _i
 _lib.ulys_strerror.argtypes = [_i]
 _lib.ulys_strerror.restype = ctypes.c_char_p
 _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_strerror", "ulys_last_error")
+EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_strerror",
+            "ulys_last_error")
 
 
 @dataclass(frozen=True)
@@ -200,6 +205,46 @@ def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_s
     oa = _ptrs(o_shards, "o_shards", _BF16, L.batch * L.shard_rows * L.hq * L.head_dim)
     c = L.c_struct()
     _check(_lib.ulys_unpack(ctypes.byref(c), rank, group, sp, oa, _stream(stream)))
+
+
+def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, q_slots, k_slots, v_slots,
+                       o_slots, o_shards, lse: torch.Tensor | None = None, softmax_scale: float = 0.0,
+                       key_gaps=None, qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None,
+                       stream=None, copy_stream=None) -> None:
+    """Pack, attend and unpack every head group of ``rank``; repack on ``copy_stream`` overlaps attention.
+
+    Slots hold all G groups (``[G, B, rows, Gh, D]``), lse ``[G, B, Gq, rows]`` or None.
+    ``copy_stream`` None means the same stream as ``stream`` (sequential).
+    """
+    L = layout
+    if len(q_shards) != L.degree or len(k_shards) != L.degree or len(v_shards) != L.degree:
+        raise ValueError("need one shard per rank for q, k and v")
+    if len(o_shards) != L.degree:
+        raise ValueError("need one output shard per rank")
+    G = L.groups
+    nq = L.batch * L.shard_rows * L.hq * L.head_dim
+    nkv = L.batch * L.shard_rows * L.hkv * L.head_dim
+    qa = _ptrs(q_shards, "q_shards", _BF16, nq)
+    ka = _ptrs(k_shards, "k_shards", _BF16, nkv)
+    va = _ptrs(v_shards, "v_shards", _BF16, nkv)
+    qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
+    qs = _dev(q_slots, "q_slots", qk_t, G * L.batch * L.rows * L.gq * L.head_dim)
+    ks = _dev(k_slots, "k_slots", qk_t, G * L.batch * L.rows * L.gkv * L.head_dim)
+    vs = _dev(v_slots, "v_slots", _BF16, G * L.batch * L.rows * L.gkv * L.head_dim)
+    os_ = _dev(o_slots, "o_slots", _BF16, G * L.batch * L.rows * L.gq * L.head_dim)
+    oa = _ptrs(o_shards, "o_shards", _BF16, nq)
+    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), G * L.batch * L.gq * L.rows)
+    am = None if qk_amax is None else _dev(qk_amax, "qk_amax", (torch.float32,), 2)
+    gaps = None
+    if key_gaps is not None:
+        if len(key_gaps) != L.batch:
+            raise ValueError("key_gaps needs one (start, end) per batch")
+        gaps = (ctypes.c_int32 * (2 * L.batch))(*[int(x) for g in key_gaps for x in g])
+    s = _stream(stream)
+    x = s if copy_stream is None else _stream(copy_stream)
+    c = L.c_struct()
+    _check(_lib.ulys_rank_pipeline(ctypes.byref(c), rank, qa, ka, va, qs, ks, vs, os_, lp, oa, qk_dtype, am,
+                                   float(softmax_scale), gaps, s, x))
 
 
 def call_raw(name: str, *args) -> int:
