@@ -79,6 +79,27 @@ def measured_traffic(groups: int):
     return entry["hbm_bytes_per_launch"]
 
 
+def merge_gbs(torch, ulys, o_slots, lse, steps: int) -> float:
+    """ulys_lse_merge of the first two head-group outputs as two partial results (a ring of two):
+    algorithmic bytes (two partial o + lse read, one o + lse written) over the mean event time."""
+    G = o_slots.shape[0]
+    if G < 2:
+        return float("nan")
+    parts, lparts = [o_slots[0], o_slots[1]], [lse[0], lse[1]]
+    out = torch.empty_like(o_slots[0])
+    lout = torch.empty_like(lse[0])
+    ulys.ulys_lse_merge(parts, lparts, out, lout)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        ulys.ulys_lse_merge(parts, lparts, out, lout)
+    e1.record()
+    torch.cuda.synchronize()
+    nbytes = 3 * (out.numel() * 2 + lout.numel() * 4)
+    return nbytes / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+
+
 def device_copy_gbs(torch) -> float:
     """Practical HBM ceiling for a stream: a plain 1 GiB device-to-device copy
     (torch copy_), read + write bytes over the median of 5 timed copies."""
@@ -262,6 +283,7 @@ def main():
                      "traffic": measured_traffic(G), "kernel": "attn_fwd_kernel<128,false>",
                      "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
     }
+    res["lse_merge_gbs"] = round(merge_gbs(torch, ulys, os_, lse, args.steps), 1)
     res["hbm_copy_gbs"] = round(device_copy_gbs(torch), 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_rows)

@@ -7,7 +7,8 @@
  *   ulys_attend_group  dense non-causal attention + log-sum-exp on one slot
  *   ulys_unpack        output slot -> output shards
  * plus ulys_rank_pipeline (the three steps for every head group of a rank,
- * repack overlapping attention on a second stream), ulys_amax_bf16
+ * repack overlapping attention on a second stream), ulys_lse_merge (merge of
+ * partial results over key blocks, for ring / hybrid parallelism), ulys_amax_bf16
  * (per-tensor fp8 scale source), ulys_strerror and ulys_last_error.
  *
  * Conventions shared by every call
@@ -115,6 +116,37 @@ int ulys_pack(const ulys_layout* layout, int rank, int group,
               const void* const* v_shards,
               void* q_slot, void* k_slot, void* v_slot,
               int qk_dtype, const float* qk_amax, void* stream);
+
+/*
+ * ulys_lse_merge -- merge the partial results of attention over disjoint key
+ * blocks into the result over all of them.
+ *
+ * Source: flashdreams cp.py, ContextParallelAttention._impl_ring (ring
+ * attention over the CP ranks' key blocks: each step's (out, lse) is absorbed
+ * with out = prev - sigmoid(lse - prev_lse) * (prev - out) and
+ * lse = prev_lse - logsigmoid(prev_lse - lse), in float32 when
+ * convert_to_fp32); the Ulysses + ring hybrid of sglang's USPAttention uses
+ * the same merge across its ring dimension.
+ *
+ * For every b, head h, row i:  L = ln sum_p exp(lse_p),
+ *   o_out = sum_p exp(lse_p - L) * o_p,  lse_out = L
+ * (the closed form of absorbing the parts one after the other), in float32,
+ * o_out rounded to bf16 (nearest even).  A part with lse = -inf (no valid key
+ * in its block) has weight 0; a row whose parts are all -inf gets o = 0 and
+ * lse = -inf.
+ *
+ * o_parts: host array of n_parts device pointers, each [B, rows, heads, D]
+ * bf16 (the o of ulys_attend_group); lse_parts: host array of n_parts device
+ * pointers, each [B, heads, rows] float32 (its lse).  o_out: [B, rows, heads,
+ * D] bf16, may be one of o_parts (each element is read before it is written);
+ * lse_out: [B, heads, rows] float32 or NULL, not one of lse_parts.
+ * Rules (ULYS_EINVAL otherwise): 1 <= n_parts <= 16; batch, rows, heads >= 1;
+ * head_dim a multiple of 8 in [8, 1024]; o pointers 16-byte aligned, lse
+ * pointers 4-byte aligned, none NULL (lse_out may be).
+ */
+int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* lse_parts,
+                   int batch, int rows, int heads, int head_dim,
+                   void* o_out, float* lse_out, void* stream);
 
 /*
  * ulys_amax_bf16 -- amax_out[0] = max |x| over n_tensors bf16 device arrays

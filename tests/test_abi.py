@@ -28,8 +28,8 @@ def _declared():
 
 def test_header_declares_the_path():
     names = _declared()
-    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_amax_bf16",
-              "ulys_strerror", "ulys_last_error"):
+    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
+              "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
         assert n in names
 
 
@@ -158,6 +158,25 @@ def test_pipeline_rules(U):
     assert "no valid key" in U.last_error()
     assert _pipeline(U, dict(GOOD, head_dim=96)) == -2
     assert _pipeline(U, dict(GOOD, hq=4 * 65, hkv=4 * 65, groups=65)) == -2   # more than 64 groups
+
+
+def _merge(U, n=2, o=None, lse=None, b=1, rows=10, heads=2, d=64, out=FAKE, lse_out=None):
+    o = _arr(n) if o is None else o
+    lse = _arr(n) if lse is None else lse
+    return U.call_raw("ulys_lse_merge", n, o, lse, b, rows, heads, d, out, lse_out, None)
+
+
+def test_merge_rules(U):
+    assert _merge(U, n=0) == -1
+    assert _merge(U, n=17, o=_arr(17), lse=_arr(17)) == -1
+    assert _merge(U, rows=0) == -1
+    assert _merge(U, d=12) == -1
+    assert _merge(U, d=2048) == -1
+    assert _merge(U, o=_arr(2, MIS)) == -1
+    assert _merge(U, lse=_arr(2, FAKE + 2)) == -1
+    assert _merge(U, out=None) == -1
+    assert _merge(U, lse_out=FAKE) == -1                     # lse_out is one of the lse parts
+    assert "lse_out" in U.last_error()
 
 
 def test_strerror(U):

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libulys.so")
-SOURCES = ["api.hip", "repack.hip", "attn.hip"]
+SOURCES = ["api.hip", "repack.hip", "attn.hip", "merge.hip"]
 # per-source flags: the attention kernel interleaves MFMA and VALU work best
 # under the ILP-maximising machine scheduler
 SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}

@@ -342,6 +342,41 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
   return hip_status(e);
 }
 
+int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* lse_parts, int batch, int rows,
+                   int heads, int head_dim, void* o_out, float* lse_out, void* stream) {
+  if (n_parts < 1 || n_parts > ulys::kMaxMergeParts)
+    return fail(ULYS_EINVAL, "n_parts %d outside [1, %d]", n_parts, ulys::kMaxMergeParts);
+  if (batch < 1 || rows < 1 || heads < 1) return fail(ULYS_EINVAL, "batch, rows and heads must be >= 1");
+  if (head_dim < 8 || head_dim > 1024 || head_dim % 8)
+    return fail(ULYS_EINVAL, "head_dim %d must be a multiple of 8 in [8, 1024]", head_dim);
+  if ((long long)batch * rows * heads * head_dim > (1LL << 40)) return fail(ULYS_EINVAL, "tensor too large");
+  int st;
+  if ((st = check_ptr_array(o_parts, n_parts, "o_parts"))) return st;
+  if (lse_parts == nullptr) return fail(ULYS_EINVAL, "lse_parts pointer array is NULL");
+  for (int i = 0; i < n_parts; ++i) {
+    if (lse_parts[i] == nullptr) return fail(ULYS_EINVAL, "lse_parts[%d] is NULL", i);
+    if ((uintptr_t)lse_parts[i] & 3u) return fail(ULYS_EINVAL, "lse_parts[%d] is not 4-byte aligned", i);
+    if (lse_out != nullptr && lse_out == lse_parts[i])
+      return fail(ULYS_EINVAL, "lse_out must not be one of the lse parts");
+  }
+  if ((st = check_ptr(o_out, "o_out"))) return st;
+  if (lse_out != nullptr && ((uintptr_t)lse_out & 3u)) return fail(ULYS_EINVAL, "lse_out is not 4-byte aligned");
+  ulys::MergeArgs a;
+  memset(&a, 0, sizeof a);
+  for (int i = 0; i < n_parts; ++i) {
+    a.o[i] = (const uint16_t*)o_parts[i];
+    a.lse[i] = lse_parts[i];
+  }
+  a.n = n_parts;
+  a.out = (uint16_t*)o_out;
+  a.lse_out = lse_out;
+  a.batch = batch;
+  a.rows = rows;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  return hip_status(ulys::launch_lse_merge(a, (hipStream_t)stream));
+}
+
 const char* ulys_strerror(int status) {
   switch (status) {
     case ULYS_OK: return "ok";

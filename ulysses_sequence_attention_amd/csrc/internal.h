@@ -10,6 +10,7 @@ namespace ulys {
 constexpr int kMaxDegree = 64;      // P shards per call (kernel-argument arrays)
 constexpr int kMaxGapBatch = 256;   // batches that may carry a key gap
 constexpr int kMaxPipelineGroups = 64;   // head groups of one ulys_rank_pipeline call
+constexpr int kMaxMergeParts = 16;       // partial results of one ulys_lse_merge call
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.
@@ -43,6 +44,15 @@ struct AmaxArgs {
   unsigned int* out;                   // float bits of max |x|
 };
 
+struct MergeArgs {
+  const uint16_t* o[kMaxMergeParts];   // partial outputs [B, rows, heads, D] bf16
+  const float* lse[kMaxMergeParts];    // partial LSEs [B, heads, rows]
+  int n;
+  uint16_t* out;                       // merged output
+  float* lse_out;                      // merged LSE or null
+  int batch, rows, heads, head_dim;
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -60,5 +70,6 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, hipStream_t s);
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace ulys

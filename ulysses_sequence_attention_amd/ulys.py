@@ -50,13 +50,15 @@ _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POIN
                                     ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _i, _vp,
                                     ctypes.c_float, _vp, _vp, _vp]
 _lib.ulys_rank_pipeline.restype = _i
+_lib.ulys_lse_merge.argtypes = [_i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _i, _i, _i, _vp, _vp, _vp]
+_lib.ulys_lse_merge.restype = _i
 _lib.ulys_strerror.argtypes = [_i]
 _lib.ulys_strerror.restype = ctypes.c_char_p
 _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_strerror",
-            "ulys_last_error")
+EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
+            "ulys_strerror", "ulys_last_error")
 
 
 @dataclass(frozen=True)
@@ -245,6 +247,21 @@ def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, 
     c = L.c_struct()
     _check(_lib.ulys_rank_pipeline(ctypes.byref(c), rank, qa, ka, va, qs, ks, vs, os_, lp, oa, qk_dtype, am,
                                    float(softmax_scale), gaps, s, x))
+
+
+def ulys_lse_merge(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tensor | None = None,
+                   stream=None) -> None:
+    """Merge partial attention results over disjoint key blocks: o ``[B, rows, heads, D]`` bf16,
+    lse ``[B, heads, rows]`` fp32 per part -> o_out (and lse_out)."""
+    if len(o_parts) != len(lse_parts) or not o_parts:
+        raise ValueError("need one lse per partial output and at least one part")
+    b, rows, heads, d = o_out.shape
+    n = b * rows * heads * d
+    oa = _ptrs(o_parts, "o_parts", _BF16, n)
+    la = _ptrs(lse_parts, "lse_parts", (torch.float32,), b * heads * rows)
+    op = _dev(o_out, "o_out", _BF16, n)
+    lp = None if lse_out is None else _dev(lse_out, "lse_out", (torch.float32,), b * heads * rows)
+    _check(_lib.ulys_lse_merge(len(o_parts), oa, la, b, rows, heads, d, op, lp, _stream(stream)))
 
 
 def call_raw(name: str, *args) -> int:
