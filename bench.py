@@ -80,12 +80,13 @@ def measured_traffic(groups: int):
 
 
 def merge_gbs(torch, ulys, o_slots, lse, steps: int) -> float:
-    """ulys_lse_merge of the first two head-group outputs as two partial results (a ring of two):
-    algorithmic bytes (two partial o + lse read, one o + lse written) over the mean event time."""
+    """ulys_lse_merge of the G head-group outputs taken as G partial results of one slot shape
+    (a ring of G): algorithmic bytes (G partial o + lse read, one o + lse written) over the mean
+    event time."""
     G = o_slots.shape[0]
     if G < 2:
         return float("nan")
-    parts, lparts = [o_slots[0], o_slots[1]], [lse[0], lse[1]]
+    parts, lparts = [o_slots[g] for g in range(G)], [lse[g] for g in range(G)]
     out = torch.empty_like(o_slots[0])
     lout = torch.empty_like(lse[0])
     ulys.ulys_lse_merge(parts, lparts, out, lout)
@@ -96,7 +97,7 @@ def merge_gbs(torch, ulys, o_slots, lse, steps: int) -> float:
         ulys.ulys_lse_merge(parts, lparts, out, lout)
     e1.record()
     torch.cuda.synchronize()
-    nbytes = 3 * (out.numel() * 2 + lout.numel() * 4)
+    nbytes = (G + 1) * (out.numel() * 2 + lout.numel() * 4)
     return nbytes / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
 
 

@@ -30,34 +30,59 @@ __device__ __forceinline__ unsigned int bf16_pair(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
 }
 
+// IDX: index type (32-bit when the chunk count fits); CPR: 16-byte chunks per
+// (b, row, head) when known at compile time (0 = runtime head_dim / 8).
+template <typename IDX, int CPR>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs a) {
-  const long chunks_per_row = a.head_dim / 8;
-  const long total = (long)a.batch * a.rows * a.heads * chunks_per_row;
-  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
+  const IDX cpr = CPR ? (IDX)CPR : (IDX)(a.head_dim / 8);
+  const IDX total = (IDX)a.batch * (IDX)a.rows * (IDX)a.heads * cpr;
+  const IDX idx = (IDX)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % chunks_per_row);
-  const long r2 = idx / chunks_per_row;
-  const int h = (int)(r2 % a.heads);
-  const long br = r2 / a.heads;
-  const int row = (int)(br % a.rows);
-  const int b = (int)(br / a.rows);
+  const IDX c = idx % cpr;
+  const IDX r2 = idx / cpr;
+  const IDX h = r2 % (IDX)a.heads;
+  const IDX br = r2 / (IDX)a.heads;
+  const IDX row = br % (IDX)a.rows;
+  const IDX b = br / (IDX)a.rows;
   const size_t li = ((size_t)b * a.heads + h) * a.rows + row;
 
+  // All loads first (the LSEs and the output chunks are independent), so one
+  // memory round trip covers the thread's whole input.
+  float lv[kMaxMergeParts];
+  u32x4 xs[kMaxMergeParts];
+#pragma unroll
+  for (int i = 0; i < kMaxMergeParts; ++i) {
+    if (i < a.n) {
+      lv[i] = a.lse[i][li];
+      xs[i] = ((const u32x4*)a.o[i])[idx];
+    }
+  }
   float m = -INFINITY;
-  for (int i = 0; i < a.n; ++i) m = fmaxf(m, a.lse[i][li]);
+#pragma unroll
+  for (int i = 0; i < kMaxMergeParts; ++i)
+    if (i < a.n) m = fmaxf(m, lv[i]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
   if (m != -INFINITY) {
     float s = 0.0f;
-    for (int i = 0; i < a.n; ++i) s += expf(a.lse[i][li] - m);
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+      if (i < a.n) {
+        lv[i] = expf(lv[i] - m);
+        s += lv[i];
+      }
+    }
     const float inv = 1.0f / s;
-    for (int i = 0; i < a.n; ++i) {
-      const float w = expf(a.lse[i][li] - m) * inv;
-      const u32x4 x = ((const u32x4*)a.o[i])[idx];
-      acc[0] += w * bf16_lo(x.x); acc[1] += w * bf16_hi(x.x);
-      acc[2] += w * bf16_lo(x.y); acc[3] += w * bf16_hi(x.y);
-      acc[4] += w * bf16_lo(x.z); acc[5] += w * bf16_hi(x.z);
-      acc[6] += w * bf16_lo(x.w); acc[7] += w * bf16_hi(x.w);
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+      if (i < a.n) {
+        const float w = lv[i] * inv;
+        const u32x4 x = xs[i];
+        acc[0] += w * bf16_lo(x.x); acc[1] += w * bf16_hi(x.x);
+        acc[2] += w * bf16_lo(x.y); acc[3] += w * bf16_hi(x.y);
+        acc[4] += w * bf16_lo(x.z); acc[5] += w * bf16_hi(x.z);
+        acc[6] += w * bf16_lo(x.w); acc[7] += w * bf16_hi(x.w);
+      }
     }
     L = m + logf(s);
   }
@@ -74,8 +99,15 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(MergeArgs a) {
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   const long total = (long)a.batch * a.rows * a.heads * (a.head_dim / 8);
-  const long blocks = (total + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+  if (total >= (1L << 32) - kThreads)
+    hipLaunchKernelGGL((lse_merge_kernel<size_t, 0>), grid, dim3(kThreads), 0, s, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((lse_merge_kernel<unsigned, 16>), grid, dim3(kThreads), 0, s, a);
+  else if (a.head_dim == 64)
+    hipLaunchKernelGGL((lse_merge_kernel<unsigned, 8>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<unsigned, 0>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
