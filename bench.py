@@ -41,6 +41,9 @@ def parse():
                          "instead of the one-stream step (pack all groups, attend each, unpack all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows the oracle computes for cpu_baseline")
+    ap.add_argument("--group-sweep", action="store_true",
+                    help="time a rank's 10 heads (D=128) as G = 1, 2, 5, 10 attention calls for several sequence "
+                         "lengths and print the automatic group count beside (calibrates ulys_auto_groups)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (HBM byte-counter calibration)")
     return ap.parse_args()
@@ -120,6 +123,39 @@ def device_copy_gbs(torch) -> float:
     return 2 * n / (sorted(times)[2] * 1e-3) / 1e9
 
 
+def group_sweep():
+    """One JSON line per sequence length: attention time of 10 heads split into G calls, and the
+    group count ulys_auto_groups picks for that shape (Wan-like layout, Ulysses degree 4)."""
+    import torch
+    from ulysses_sequence_attention_amd import ulys
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    for rows in (2048, 4096, 8192, 16384, 27280):
+        times = {}
+        for gh in (10, 5, 2, 1):
+            G = 10 // gh
+            q = torch.randn((G, 1, rows, gh, 128), generator=gen).to(torch.bfloat16).cuda()
+            k, v = q.roll(1, dims=2), q.roll(2, dims=2)
+            o = torch.empty_like(q)
+            lse = torch.empty((G, 1, gh, rows), device="cuda")
+            run = lambda: [ulys.ulys_attend_group(q[g], k[g], v[g], o[g], lse[g]) for g in range(G)]
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            times[G] = e0.elapsed_time(e1) / 10
+        L = ulys.Layout(1, 4, rows // 4, 0, True, 40, 40, 128, 1)
+        print(json.dumps({"rows": rows, "heads": 10, "cus": cus,
+                          "ms_by_groups": {str(G): round(t, 4) for G, t in sorted(times.items())},
+                          "relative_to_one_call": {str(G): round(t / times[1], 3) for G, t in sorted(times.items())},
+                          "auto_groups": ulys.ulys_auto_groups(L, cus)}), flush=True)
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB, five times: reads 1 GiB and
     writes 1 GiB per launch.  Run under `rocprofv3 --pmc FETCH_SIZE` (then
@@ -166,6 +202,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.group_sweep:
+        group_sweep()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",

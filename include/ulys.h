@@ -149,6 +149,25 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
                    void* o_out, float* lse_out, void* stream);
 
 /*
+ * ulys_auto_groups -- the head-group count for ulys_rank_pipeline on this GPU.
+ *
+ * Source: sglang PR #43521, "Automatic group count" (the largest of 7, 5, 4,
+ * 3 and 2 that divides the q and k/v heads per rank while each group's call
+ * still fills the GPU; otherwise no split -- calls too small to fill the
+ * device cost more than the overlap saves).
+ *
+ * The fill test is MI355X's, re-measured for this library's attention (one
+ * 256-row workgroup per CU at a time, so a call runs in rounds of
+ * compute_units workgroups and a partial round costs nearly a full one): G is
+ * accepted when G calls take no more rounds than the one call over all the
+ * rank's heads, i.e. G * ceil(W / G / cus) <= ceil(W / cus) with
+ * W = batch * (Hq/P) * ceil(rows / 256).  Returns the count (>= 1; 1 = keep
+ * the sequential single call); layout->groups is ignored.
+ * Rules: the layout rules with groups = 1; compute_units >= 1 (ULYS_EINVAL).
+ */
+int ulys_auto_groups(const ulys_layout* layout, int compute_units);
+
+/*
  * ulys_amax_bf16 -- amax_out[0] = max |x| over n_tensors bf16 device arrays
  * of elems_each elements each (the per-tensor fp8 scale source; exact,
  * independent of order).  amax_out is a device float, overwritten.

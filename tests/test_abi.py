@@ -29,7 +29,7 @@ def _declared():
 def test_header_declares_the_path():
     names = _declared()
     for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
-              "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
+              "ulys_auto_groups", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
         assert n in names
 
 
@@ -177,6 +177,34 @@ def test_merge_rules(U):
     assert _merge(U, out=None) == -1
     assert _merge(U, lse_out=FAKE) == -1                     # lse_out is one of the lse parts
     assert "lse_out" in U.last_error()
+
+
+def _groups(U, **kw):
+    L = dict(batch=1, degree=4, s_local=6820, n_rep=0, rep_first=True, hq=40, hkv=40, head_dim=128, groups=1)
+    L.update(kw)
+    return U.ulys_auto_groups(U.Layout(**L), kw.pop("cus", 256) if "cus" in kw else 256)
+
+
+def test_auto_groups_follow_the_rounds_rule(U):
+    """Wan2.1 at Ulysses 4 (27280 rows, 10 heads per rank): one call takes ceil(1070/256) = 5
+    rounds of workgroups, five 2-head calls 5 x 1 -> 5 groups.  Measured on MI355X (group-split
+    sweep): 16384 rows (3 rounds) gets no split, 8192 rows (2 rounds) splits in two."""
+    assert _groups(U) == 5
+    assert _groups(U, s_local=16384 // 4) == 1
+    assert _groups(U, s_local=8192 // 4) == 2
+    assert _groups(U, s_local=1024) == 1                               # small image: one call
+    assert _groups(U, groups=3) == 5                                   # the layout's own count is ignored
+    # 12 heads per rank, 32760 rows: W = 12 x 128 = 1536 -> 6 rounds; 7 and 5 do not divide 12,
+    # 4 groups take 4 x 2 = 8 rounds, 3 groups 3 x 2 = 6
+    assert _groups(U, hq=48, hkv=48, s_local=8190) == 3
+    # GQA 40/8 at P 4: only 2 divides the 2 k/v heads per rank, and 2 x 3 rounds > 5
+    assert _groups(U, hq=40, hkv=8) == 1
+    assert _groups(U, hq=40, hkv=8, s_local=8192 // 4) == 2
+    assert U.call_raw("ulys_auto_groups", None, 256) == -1
+    c = U.Layout(**dict(GOOD)).c_struct()
+    assert U.call_raw("ulys_auto_groups", ctypes.byref(c), 0) == -1
+    c.hq = 42
+    assert U.call_raw("ulys_auto_groups", ctypes.byref(c), 256) == -1
 
 
 def test_strerror(U):

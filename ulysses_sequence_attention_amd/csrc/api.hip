@@ -377,6 +377,34 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
   return hip_status(ulys::launch_lse_merge(a, (hipStream_t)stream));
 }
 
+int ulys_auto_groups(const ulys_layout* L, int compute_units) {
+  if (compute_units < 1) return fail(ULYS_EINVAL, "compute_units must be >= 1");
+  if (L == nullptr) return fail(ULYS_EINVAL, "layout is NULL");
+  ulys_layout one = *L;                 // every layout rule except the group count itself
+  one.groups = 1;
+  const int st = check_layout(&one, 0, -1);
+  if (st) return st;
+  const long long rows = (long long)L->n_rep + (long long)L->degree * L->s_local;
+  const long long hq_rank = L->hq / L->degree, hkv_rank = L->hkv / L->degree;
+  // Workgroups of the one-call attention (256 query rows each, one per CU at
+  // a time) and the rounds of CUs they take.
+  const long long wgs = (long long)L->batch * hq_rank * ((rows + ulys::kAttnRowsPerWorkgroup - 1) /
+                                                        ulys::kAttnRowsPerWorkgroup);
+  const long long rounds_one = (wgs + compute_units - 1) / compute_units;
+  static const int kCandidates[] = {7, 5, 4, 3, 2};
+  for (int G : kCandidates) {
+    if (hq_rank % G || hkv_rank % G) continue;
+    const long long per_call = wgs / G;
+    const long long rounds = G * ((per_call + compute_units - 1) / compute_units);
+    if (rounds <= rounds_one) {
+      ok();
+      return G;
+    }
+  }
+  ok();
+  return 1;
+}
+
 const char* ulys_strerror(int status) {
   switch (status) {
     case ULYS_OK: return "ok";

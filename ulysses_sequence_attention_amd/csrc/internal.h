@@ -11,6 +11,7 @@ constexpr int kMaxDegree = 64;      // P shards per call (kernel-argument arrays
 constexpr int kMaxGapBatch = 256;   // batches that may carry a key gap
 constexpr int kMaxPipelineGroups = 64;   // head groups of one ulys_rank_pipeline call
 constexpr int kMaxMergeParts = 16;       // partial results of one ulys_lse_merge call
+constexpr int kAttnRowsPerWorkgroup = 256;   // query rows per attention workgroup (one per CU at a time)
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.

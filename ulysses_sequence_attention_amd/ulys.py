@@ -52,13 +52,15 @@ _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POIN
 _lib.ulys_rank_pipeline.restype = _i
 _lib.ulys_lse_merge.argtypes = [_i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.ulys_lse_merge.restype = _i
+_lib.ulys_auto_groups.argtypes = [ctypes.POINTER(ulys_layout), _i]
+_lib.ulys_auto_groups.restype = _i
 _lib.ulys_strerror.argtypes = [_i]
 _lib.ulys_strerror.restype = ctypes.c_char_p
 _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
-            "ulys_strerror", "ulys_last_error")
+            "ulys_auto_groups", "ulys_strerror", "ulys_last_error")
 
 
 @dataclass(frozen=True)
@@ -262,6 +264,14 @@ def ulys_lse_merge(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tenso
     op = _dev(o_out, "o_out", _BF16, n)
     lp = None if lse_out is None else _dev(lse_out, "lse_out", (torch.float32,), b * heads * rows)
     _check(_lib.ulys_lse_merge(len(o_parts), oa, la, b, rows, heads, d, op, lp, _stream(stream)))
+
+
+def ulys_auto_groups(layout: Layout, compute_units: int = 256) -> int:
+    """Head-group count for ulys_rank_pipeline (1 = keep one call); ``layout.groups`` is ignored."""
+    c = layout.c_struct()
+    st = _lib.ulys_auto_groups(ctypes.byref(c), int(compute_units))
+    _check(min(st, 0))
+    return st
 
 
 def call_raw(name: str, *args) -> int:
