@@ -15,9 +15,10 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libulys.so")
 SOURCES = ["api.hip", "repack.hip", "attn.hip", "merge.hip"]
-# per-source flags: the attention kernel interleaves MFMA and VALU work best
-# under the ILP-maximising machine scheduler
-SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# per-source flags: the attention kernel never relies on NaN semantics (inputs
+# must be finite; masked scores are -inf), so its max reductions need no
+# canonicalising instructions
+SOURCE_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
 _EXTRA: list = []
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -20,24 +20,29 @@
 //    gfx950's transposing LDS read (ds_read_b64_tr_b16: within 16 lanes, four
 //    8-byte row pieces are returned as columns), so V is never transposed in
 //    registers or written element by element.
-//  * 64-key tiles, double-buffered in LDS and filled by direct global->LDS
-//    16-byte loads (no staging registers): the next tile streams in while
-//    the current one is computed; one barrier per tile.
-//  * Within a tile the two 32-key blocks are software-pipelined: the QK^T
-//    MFMAs of block 1 are issued between the exp/convert instructions of
-//    block 0, and the PV MFMAs of block 0 between the row-max instructions of
-//    block 1, so each wave keeps its matrix core and vector ALU busy at once.
+//  * 64-key tiles in a three-stage LDS ring, filled by direct global->LDS
+//    16-byte loads (no staging registers) two tiles ahead; one barrier per
+//    tile.
+//  * Software pipeline over 32-key blocks: while block b's probabilities are
+//    formed (VALU), the wave issues the PV MFMAs of block b-1 and the QK^T
+//    MFMAs of block b+1, which do not depend on them; K operands of b+1 and V
+//    operands of b are read from LDS one phase before their MFMAs.
 //  * Online softmax in the exp2 domain per 32-key block with a lazy max: the
-//    running max is only raised (and O, l rescaled) when a block's max
-//    exceeds it by more than 2^8, a wave-uniform branch; probabilities stay
-//    <= 256, exact either way because the final normalisation divides by the
-//    sum built with the same max.  Row sums are fp32 sums of the unrounded
-//    probabilities (the LSE must not inherit the 2^-9 bf16 rounding of the
-//    MFMA operand).
+//    running max is only raised (and O, l rescaled) when some score of a
+//    block exceeds it by more than 8 (a factor 2^8), a wave-uniform branch
+//    taken a few times per row.  The probabilities are formed speculatively
+//    with the current max and redone from the scores (recomputed from K in
+//    LDS) only on that branch, so the check sits after the MFMAs instead of
+//    in front of the exponentials.  Probabilities stay <= 2^8, exact either
+//    way because the final normalisation divides by the sum built with the
+//    same max.  Row sums are fp32 sums of the unrounded probabilities (the
+//    LSE must not inherit the 2^-9 bf16 rounding of the MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ulys {
@@ -52,10 +57,24 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
+#ifndef ULYS_ATTN_XCD
+#define ULYS_ATTN_XCD 0
+#endif
+#ifndef ULYS_ATTN_UNROLL
+#define ULYS_ATTN_UNROLL 0
+#endif
+#ifndef ULYS_ATTN_STAGES
+#define ULYS_ATTN_STAGES 3
+#endif
+
+#ifndef ULYS_ATTN_WAVES
+#define ULYS_ATTN_WAVES 8
+#endif
+constexpr int kWaves = ULYS_ATTN_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per LDS tile (two 32-key blocks)
+constexpr int kStages = ULYS_ATTN_STAGES;     // LDS ring depth (tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
@@ -76,12 +95,10 @@ struct Cfg {
   static constexpr int kVSegs = kVTile / 1024;
   static constexpr int kKSegsPerWave = (kKSegs + kWaves - 1) / kWaves;
   static constexpr int kVSegsPerWave = (kVSegs + kWaves - 1) / kWaves;
+  static constexpr int kLoadsPerTile = kKSegsPerWave + kVSegsPerWave;   // per wave
 };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
-
-template <int S>
-struct StageTag { static constexpr int value = S; };
 
 // 8-byte chunk index of V row `key` after the swizzle: rows read together by a
 // transposing LDS read land on distinct banks.
@@ -102,6 +119,22 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
 
 #define ULYS_INLINE __attribute__((always_inline))
 
+// One 16-byte-per-lane global->LDS load (global_load_lds_dwordx4: lane i's 16
+// bytes land at LDS m0 + 16 i).  Issued as inline asm so that the compiler does
+// not treat it as an LDS store it must wait for before unrelated LDS reads of
+// other ring stages; the kernel waits for these loads itself (vmcnt) before the
+// barrier that publishes a tile.  m0 is set here and used by nothing else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gptr, unsigned int lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ unsigned int lds_u32(const void* p) {
+  return (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <int D, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -109,12 +142,14 @@ void attn_fwd_kernel(AttnArgs a) {
   // One LDS array per stage, selected at compile time: the compiler can then
   // prove that the DMA filling one stage never aliases reads of the other and
   // does not wait for in-flight tile loads before every LDS read.
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[C::kKTile];
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[C::kKTile];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[C::kVTile];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[C::kVTile];
-  auto k_of = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return k_lds0; else return k_lds1; };
-  auto v_of = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return v_lds0; else return v_lds1; };
+  // The LDS ring: three stages of one K tile and one V tile each.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * (C::kKTile + C::kVTile)];
+  // Stage st's K tile; its V tile sits at v_of(st) + the V region offset, which
+  // the per-lane V read offsets carry (so every LDS read's immediate offset
+  // stays below 64 KB).
+  auto k_of = [&](auto st) -> unsigned char* { return lds + int(st) * C::kKTile; };
+  auto v_of = [&](auto st) -> unsigned char* { return lds + int(st) * C::kVTile; };
+  constexpr int kVRegion = kStages * C::kKTile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,9 +157,26 @@ void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+#if ULYS_ATTN_XCD
+  // Workgroups are dealt to the 8 XCDs round robin (id % 8); give each XCD a
+  // contiguous run of (batch, head, query tile) so the workgroups sharing an
+  // XCD's L2 stream the same head's K/V.
+  int qtile, head, b;
+  {
+    const int nq = (a.rows + kBM - 1) / kBM;
+    const int total = nq * a.hq * a.batch;
+    const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int n = xcd * per + min(xcd, rem) + j;
+    qtile = n % nq;
+    head = (n / nq) % a.hq;
+    b = n / (nq * a.hq);
+  }
+#else
   const int qtile = blockIdx.x;
   const int head = blockIdx.y;
   const int b = blockIdx.z;
+#endif
   const int rows = a.rows;
   const int kvh = head / (a.hq / a.hkv);
 
@@ -143,11 +195,6 @@ void attn_fwd_kernel(AttnArgs a) {
   if (a.has_gap) { gs = a.gap[b][0]; ge = a.gap[b][1]; if (ge <= gs) { gs = rows; ge = rows; } }
   const int skip_first = (gs + kBN - 1) / kBN;
   const int skip_last = (ge >= rows) ? ntiles : ge / kBN;   // tiles [skip_first, skip_last) are fully masked
-  auto next_tile = [&](int j) {
-    const int n = j + 1;
-    return (n == skip_first && skip_last > n) ? skip_last : n;
-  };
-  const int first_tile = (skip_first == 0 && skip_last > 0) ? skip_last : 0;
 
   // ---- Q fragments in registers (B operand of S^T = K Q^T) ----
   const size_t q_row_stride = (size_t)a.hq * D;            // elements
@@ -181,33 +228,32 @@ void attn_fwd_kernel(AttnArgs a) {
   const unsigned char* vbase = (const unsigned char*)a.v + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * 2;
   auto load_tile = [&](int j, auto st) {
     unsigned char* kl = k_of(st);
-    unsigned char* vl = v_of(st);
+    unsigned char* vl = v_of(st) + kVRegion;
     const int k0 = j * kBN;
     constexpr int kKRowsPerSeg = 1024 / C::kKRow;
 #pragma unroll
     for (int u = 0; u < C::kKSegsPerWave; ++u) {
-      const int seg = wave + u * kWaves;
-      if (C::kKSegs % kWaves != 0 && seg >= C::kKSegs) break;   // wave-uniform
+      // every wave issues the same number of loads (a surplus wave repeats
+      // the last segment), so a wave's outstanding-load count per tile is a
+      // compile-time constant
+      const int seg = min(wave + u * kWaves, C::kKSegs - 1);
       const int key = seg * kKRowsPerSeg + lane / C::kKChunks;
       const int sck = lane % C::kKChunks;
       const int ck = sck ^ (key & (C::kKSwz - 1));
       const int grow = min(k0 + key, rows - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kbase + (size_t)grow * kv_row_stride * C::kQKBytes + ck * 16),
-          (void __attribute__((address_space(3)))*)(&kl[seg * 1024]), 16, 0, 0);
+      dma16(kbase + (size_t)grow * kv_row_stride * C::kQKBytes + ck * 16,
+            __builtin_amdgcn_readfirstlane(lds_u32(&kl[seg * 1024])));
     }
     constexpr int kVRowsPerSeg = 1024 / C::kVRow;
 #pragma unroll
     for (int u = 0; u < C::kVSegsPerWave; ++u) {
-      const int seg = wave + u * kWaves;
-      if (C::kVSegs % kWaves != 0 && seg >= C::kVSegs) break;   // wave-uniform
+      const int seg = min(wave + u * kWaves, C::kVSegs - 1);
       const int key = seg * kVRowsPerSeg + lane / C::kVChunks;
       const int sck = lane % C::kVChunks;                 // 16-byte slot in the LDS row
       const int ck = vswz<D>(key, 2 * sck) >> 1;          // its global 16-byte chunk
       const int grow = min(k0 + key, rows - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(vbase + (size_t)grow * kv_row_stride * 2 + ck * 16),
-          (void __attribute__((address_space(3)))*)(&vl[seg * 1024]), 16, 0, 0);
+      dma16(vbase + (size_t)grow * kv_row_stride * 2 + ck * 16,
+            __builtin_amdgcn_readfirstlane(lds_u32(&vl[seg * 1024])));
     }
   };
 
@@ -217,22 +263,26 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m_run = -INFINITY;              // running max of c*log2e*s (lazy)
-  float l_run0 = 0.0f, l_run1 = 0.0f;   // partial row sums (two chains)
+  float m_run = -INFINITY;   // running max of c*log2e*s (lazy)
+  float negm = 0.0f;         // -m_run, or 0 while m_run is -inf
+  float thr = -INFINITY;     // raw score above which a block raises m_run: (m_run + 8) / (c log2 e)
+  float l_run = 0.0f;        // row sum (this lane's half of the keys)
+  const float inv_c2 = 1.0f / c2;
 
-  // End of a tile: this wave's tile loads have landed and its LDS reads are
-  // done (s_waitcnt vmcnt(0) lgkmcnt(0), as a builtin so the compiler's own
-  // wait tracking knows), then all waves meet at s_barrier.  The empty asm
-  // statements keep the compiler from moving memory accesses across it.
+  // Barrier publishing the next tile: this wave's loads of that tile have
+  // landed (s_waitcnt vmcnt(N): at most the later tiles' loads still in flight;
+  // an immediate, so the count per tile is uniform across waves), then all
+  // waves meet at s_barrier.  LDS reads still in flight are of stages in use
+  // and may cross it.  The empty asm statements keep the compiler from moving
+  // memory accesses across it.
+  constexpr int kInFlight = (kStages - 3) * C::kLoadsPerTile;
+  static_assert(kInFlight < 16, "vmcnt immediate");
   auto tile_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kInFlight);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-
-  load_tile(first_tile, StageTag<0>{});
-  tile_barrier();
 
   // Per-lane LDS byte offsets of the MFMA operand reads, computed once: the
   // XOR swizzles only involve key bits that are the same for every 32-key
@@ -251,31 +301,39 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   }
   //  V (A operand of O^T, transposing reads): within 16 lanes, lane 4j+t reads
-  //  row key0 + j at head-dim d0 + 4t.. (see pv).
+  //  row key0 + j at head-dim d0 + 4t.. (see read_v).
   const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
   const int vkey0 = 4 * (g16 >> 1) + jrow;
   int voff[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db)
-    voff[db] = vkey0 * C::kVRow + vswz<D>(vkey0, db * 8 + (g16 & 1) * 4 + tcol) * 8;
+    voff[db] = kVRegion + vkey0 * C::kVRow + vswz<D>(vkey0, db * 8 + (g16 & 1) * 4 + tcol) * 8;
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) asm volatile("" : "+v"(voff[db]));   // keep the region offset in the register
 
   // ---- block pieces ----
-  // S^T for the 32 keys kb*32.. of the tile in K stage `kl`.
-  auto qk = [&](const unsigned char* kl, int kb) ULYS_INLINE {
+  struct KFrag { u32x4 x[kKOffs]; };      // K operands of one 32-key block
+  struct VFrag { bf16x8 x[C::kDB][2]; };  // V^T operands of one 32-key block
+
+  auto read_k = [&](const unsigned char* kl, auto kb, KFrag& kf) ULYS_INLINE {
+    const unsigned char* kblk = kl + int(kb) * 32 * C::kKRow;
+#pragma unroll
+    for (int i = 0; i < kKOffs; ++i) kf.x[i] = *(const u32x4*)(kblk + koff[i]);
+  };
+
+  // S^T = K Q^T for one 32-key block.
+  auto qk = [&](const KFrag& kf) ULYS_INLINE {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-    const unsigned char* kblk = kl + kb * 32 * C::kKRow;
 #pragma unroll
     for (int kk = 0; kk < C::kQKSteps; ++kk) {
       if constexpr (!FP8) {
-        const u32x4 kx = *(const u32x4*)(kblk + koff[kk]);
         const u32x4 qx = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), __builtin_bit_cast(bf16x8, qx), s,
-                                                    0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[kk]),
+                                                    __builtin_bit_cast(bf16x8, qx), s, 0, 0, 0);
       } else {
-        const u32x4 k0x = *(const u32x4*)(kblk + koff[2 * kk]);
-        const u32x4 k1x = *(const u32x4*)(kblk + koff[2 * kk + 1]);
+        const u32x4 k0x = kf.x[2 * kk], k1x = kf.x[2 * kk + 1];
         const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
                           (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
         const i32x8 bq = {(int)qf[kk][0], (int)qf[kk][1], (int)qf[kk][2], (int)qf[kk][3],
@@ -284,6 +342,31 @@ void attn_fwd_kernel(AttnArgs a) {
       }
     }
     return s;
+  };
+
+  // V^T operands of one 32-key block: lane l needs V[key(hh, i)][d = 32 db + l%32],
+  // i = 0..7, read as two transposing 8-byte loads over keys base + 4 hh + (0..3)
+  // and base + 8 + 4 hh + (0..3) -- the keys whose probabilities p[e] holds.
+  auto read_v = [&](const unsigned char* vl, auto kb, VFrag& vf) ULYS_INLINE {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const unsigned char* va_p = vl + (int(kb) * 32 + 16 * e) * C::kVRow + voff[db];
+        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
+        const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
+        vf.x[db][e] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+
+  // O^T += V^T P^T for one 32-key block.
+  auto pv = [&](const VFrag& vf, const bf16x8 (&p)[2]) ULYS_INLINE {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.x[db][e], p[e], o[db], 0, 0, 0);
   };
 
   // Tail keys and keys inside the gap -> -inf: branch-free selects under one
@@ -300,119 +383,193 @@ void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Row max of a block, in the exp2 domain.
-  auto rowmax = [&](const f32x16& s) ULYS_INLINE {
-    float m = s[0];
+  // This lane's max over its 16 scores of a block (raw scores).
+  auto part_max = [&](const f32x16& s) ULYS_INLINE {
+    float m = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
-    return lane_swap_max(m) * c2;
+    for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, s[r]), s[r + 1]);
+    return fmaxf(m, s[15]);
   };
 
-  // Lazy rescale before a block's probabilities are formed.
-  auto rescale = [&](float mx) ULYS_INLINE {
-    if (__any(mx > m_run + kLazy)) {
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
-      m_run = mn;
-      l_run0 *= alpha;
-      l_run1 *= alpha;
+  // Probabilities exp2(c log2e s - m_run) of accumulator registers 8e..8e+7
+  // -> bf16 B operand p[e] of the PV MFMA, and their fp32 sums in two chains.
+  auto probs_half = [&](const f32x16& s, int e, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, negm));
+      const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, negm));
+      const f32x2 xx = {x0, x1};
+      const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
+      p[e][2 * i] = pk[0];
+      p[e][2 * i + 1] = pk[1];
+      if (e == 0 && i == 0) { ls0 = x0; ls1 = x1; } else { ls0 += x0; ls1 += x1; }
     }
   };
-
-  // Probabilities -> bf16 B operands of the PV MFMA (p[e] = accumulator
-  // registers 8e..8e+7) and fp32 row sums.
-  auto probs = [&](const f32x16& s, bf16x8 (&p)[2]) ULYS_INLINE {
-    const float mb = (m_run == -INFINITY) ? 0.0f : m_run;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, -mb));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, -mb));
-        const f32x2 xx = {x0, x1};
-        const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
-        p[e][2 * i] = pk[0];
-        p[e][2 * i + 1] = pk[1];
-        l_run0 += x0;
-        l_run1 += x1;
-      }
+  auto probs = [&](const f32x16& s, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
+    probs_half(s, 0, p, ls0, ls1);
+    probs_half(s, 1, p, ls0, ls1);
   };
 
-  // The probabilities and row sums are complete here (the empty asm consumes
-  // them), so the compiler schedules their VALU work between the QK^T MFMAs
-  // issued before this point instead of sinking it past the mask branch.
-  auto pin = [&](const bf16x8 (&pp)[2]) ULYS_INLINE {
-    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pp[0])), "v"(__builtin_bit_cast(u32x4, pp[1])), "v"(l_run0),
-                 "v"(l_run1));
+  // The probabilities and sums are complete here (the empty asm consumes
+  // them), so the compiler keeps their VALU work among the MFMAs issued before
+  // this point instead of sinking it past the rescale branch.
+  auto pin = [&](const bf16x8 (&pp)[2], float ls0, float ls1) ULYS_INLINE {
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pp[0])), "v"(__builtin_bit_cast(u32x4, pp[1])), "v"(ls0),
+                 "v"(ls1));
   };
 
-  // O^T += V^T P^T for the 32 keys kb*32.. of the tile in V stage `vl`.  A
-  // operand of lane l: V[key(hh, i)][d = 32 db + l%32], i = 0..7, read as two
-  // transposing 8-byte loads over keys base + 4 hh + (0..3) and
-  // base + 8 + 4 hh + (0..3) -- the keys whose probabilities p[e] holds.
-  auto pv = [&](const unsigned char* vl, int kb, const bf16x8 (&p)[2]) ULYS_INLINE {
+  // Raising the running max (rare: a few times per row).  The PV MFMAs of the
+  // previous block were formed with the old max and are already accumulated,
+  // so O and l are rescaled by exp2(m_old - m_new); then this block's scores
+  // are recomputed from K in LDS and its probabilities redone with the new max.
+  auto raise_max = [&](float pm, const unsigned char* kl, int kb, int kb0, bf16x8 (&p)[2], float& ls0,
+                       float& ls1) ULYS_INLINE {
+    const float mx = lane_swap_max(pm) * c2;
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
+    m_run = mn;
+    negm = (mn == -INFINITY) ? 0.0f : -mn;
+    thr = (mn == -INFINITY) ? -INFINITY : (mn + kLazy) * inv_c2;
+    l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) {
+    for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const unsigned char* va_p = vl + (kb * 32 + 16 * e) * C::kVRow + voff[db];
-        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
-        const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
-        const bf16x8 af = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, p[e], o[db], 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    KFrag kf;
+    read_k(kl, kb, kf);
+    f32x16 s = qk(kf);
+    mask(s, kb0);
+    probs(s, p, ls0, ls1);
+  };
+
+  // ---- software pipeline over 32-key blocks ----
+  // Iteration b holds S(b) (scores), the V^T operands of block b-1 and its
+  // probabilities P(b-1).  It issues the K reads of block b+1, forms P(b)
+  // speculatively with the current max (VALU), accumulates PV(b-1) and computes
+  // S(b+1) (MFMA, independent of the softmax of b), reads V(b), and only then
+  // checks whether block b raises the max.  The LDS ring has three stages: a
+  // tile is read from the iteration before its first block to its last block.
+  // Scores and probabilities alternate between two register sets from one
+  // block to the next (S(b) in one, S(b+1) in the other), so no copies.
+  f32x16 sA, sB;
+  VFrag vf;
+  bf16x8 pA[2], pB[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pA[e][i] = (__bf16)0.0f;
+
+  // Instruction order of one scheduling phase: `lead` LDS reads first (their
+  // fragments are consumed one phase later), then each MFMA followed by `ds`
+  // LDS reads and `valu` vector instructions (masks: 0x8 MFMA, 0x100 DS read,
+  // 0x2 VALU).
+  auto interleave = [&](auto lead, auto n_mfma, auto ds, auto valu) ULYS_INLINE {
+    if constexpr (decltype(lead)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(lead)::value, 0);
+#pragma unroll
+    for (int i = 0; i < decltype(n_mfma)::value; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(ds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds)::value, 0);
+      if constexpr (decltype(valu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(valu)::value, 0);
     }
   };
+  constexpr int kPVMfma = 2 * C::kDB;
+  constexpr int kQKMfma = C::kQKSteps;
+  constexpr int kVReads = 4 * C::kDB;
 
-  // One tile, software-pipelined over its two blocks:
-  //   QK 0, mask/max/rescale 0 | {QK 1 + probabilities 0} | mask 1 |
-  //   {PV 0 + row max 1} | rescale 1, probabilities 1, PV 1.
-  auto compute_tile = [&](int j, auto st) {
-    const unsigned char* kl = k_of(st);
-    const unsigned char* vl = v_of(st);
-    const int k0 = j * kBN;
-    bf16x8 p[2];
-    f32x16 s0 = qk(kl, 0);
-    mask(s0, k0);
-    rescale(rowmax(s0));
-    f32x16 s1 = qk(kl, 1);
-    probs(s0, p);
-    pin(p);
-    mask(s1, k0 + 32);
-    pv(vl, 0, p);
-    const float m1 = rowmax(s1);
-    rescale(m1);
-    probs(s1, p);
-    pv(vl, 1, p);
+  // Block b: s_in = S(b), p_in = P(b-1), vf = V(b-1) operands.  Produces
+  // s_out = S(b+1) (K of stage st_next, block kb_next), p_out = P(b), and
+  // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b.
+  auto iteration = [&](auto st_next, auto kb_next, auto st, auto kb, int kb0, f32x16& s_in, f32x16& s_out,
+                       bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
+    mask(s_in, kb0);
+    // phase 1: K reads of block b+1; PV(b-1) MFMAs under the row max and the
+    // first half of the probabilities of block b
+    KFrag kf;
+    read_k(k_of(st_next), kb_next, kf);
+    const float pm = part_max(s_in);
+    float ls0, ls1;
+    probs_half(s_in, 0, p_out, ls0, ls1);
+    pv(vf, p_in);
+    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, kPVMfma>{},
+               std::integral_constant<int, 0>{}, std::integral_constant<int, (8 + 26 + kPVMfma - 1) / kPVMfma>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 2: V reads of block b (into the registers PV(b-1) just consumed);
+    // QK(b+1) MFMAs under the second half of the probabilities
+    read_v(v_of(st), kb, vf);
+    s_out = qk(kf);
+    probs_half(s_in, 1, p_out, ls0, ls1);
+    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, kQKMfma>{},
+               std::integral_constant<int, (kVReads + kQKMfma - 1) / kQKMfma>{},
+               std::integral_constant<int, (29 + kQKMfma - 1) / kQKMfma>{});
+    pin(p_out, ls0, ls1);
+    if (__any(pm > thr)) raise_max(pm, k_of(st), kb, kb0, p_out, ls0, ls1);
+    l_run += ls0 + ls1;
   };
 
-  // Tiles alternate between the two stages; the next tile's loads are issued
-  // before the current tile is computed.
-  for (int j = first_tile;;) {
-    int jn = next_tile(j);
-    if (jn < ntiles) load_tile(jn, StageTag<1>{});
-    compute_tile(j, StageTag<0>{});
-    tile_barrier();
-    if (jn >= ntiles) break;
-    j = jn;
-    jn = next_tile(j);
-    if (jn < ntiles) load_tile(jn, StageTag<0>{});
-    compute_tile(j, StageTag<1>{});
-    tile_barrier();
-    if (jn >= ntiles) break;
-    j = jn;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // Tiles in processing order: all tiles except those wholly inside the gap.
+  const int nskip = max(0, skip_last - skip_first);
+  const int nseq = ntiles - nskip;
+  auto seq_tile = [&](int pos) { return pos < skip_first ? pos : pos + nskip; };
+  // Position pos goes to stage pos % kStages; past the end the last tile is
+  // loaded again, which keeps every wave's load count per tile uniform.
+  auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, nseq - 1)), st); };
+
+  load_pos(0, std::integral_constant<int, 0>{});
+  load_pos(1, std::integral_constant<int, 1>{});
+  if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  {
+    KFrag kf;
+    read_k(k_of(B0{}), B0{}, kf);
+    sA = qk(kf);
+    read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
   }
+  int tc = seq_tile(0);
+  iteration(B0{}, B1{}, B0{}, B0{}, tc * kBN, sA, sB, pA, pB);
+  tile_barrier();
+
+  // Position i (stage SA): its second block, then the first block of
+  // position i+1 (stage SB).  Position i + kStages - 1 is loaded first, into
+  // SP, the stage of position i-1, which every wave has finished with.  Each
+  // step ends with a barrier.  Returns false after the last position.
+  auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
+    load_pos(i + kStages - 1, SP);
+    iteration(SB, B0{}, SA, B1{}, tc * kBN + 32, sB, sA, pB, pA);
+    if (i + 1 >= nseq) return false;
+    tc = seq_tile(i + 1);
+    iteration(SB, B1{}, SB, B0{}, tc * kBN, sA, sB, pA, pB);
+    tile_barrier();
+    return true;
+  };
+#if ULYS_ATTN_UNROLL
+  static_assert(kStages == 3, "unrolled ring");
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  for (int i = 0;; i += 3) {
+    if (!step(i, S0{}, S1{}, S2{})) break;
+    if (!step(i + 1, S1{}, S2{}, S0{})) break;
+    if (!step(i + 2, S2{}, S0{}, S1{})) break;
+  }
+#else
+  int sa = 0;
+  for (int i = 0;; ++i) {
+    const int sb = sa == kStages - 1 ? 0 : sa + 1;
+    if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
+    sa = sb;
+  }
+#endif
+  pv(vf, pA);
 
   // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
   {
     const int row = qrow0 + l32;
-    const float l = lane_swap_sum(l_run0 + l_run1);
+    const float l = lane_swap_sum(l_run);
     const float inv = 1.0f / l;
     if (row < rows) {
       uint16_t* op = a.o + ((size_t)b * rows + row) * q_row_stride + (size_t)head * D;
@@ -437,7 +594,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool FP8>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
+#if ULYS_ATTN_XCD
+  dim3 grid(((a.rows + kBM - 1) / kBM) * a.hq * a.batch);
+#else
   dim3 grid((a.rows + kBM - 1) / kBM, a.hq, a.batch);
+#endif
   hipLaunchKernelGGL((attn_fwd_kernel<D, FP8>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
