@@ -67,7 +67,9 @@ typedef enum {
  * n_rep >= 0; rep_first in {0, 1}; P | Hq and P | Hkv (flashdreams cp.py,
  * ContextParallelAttention._impl_ulysses: heads must divide by the CP size);
  * Hkv | Hq (GQA); G | Hq/P and G | Hkv/P (sglang PR #43521, "Automatic group
- * count": a group count must divide the q and k/v heads per rank).
+ * count": a group count must divide the q and k/v heads per rank); a q slot
+ * batch * rows * (Hq/(P*G)) * head_dim * 2 bytes holds fewer than 2^32 16-byte
+ * chunks (64 GiB; the repack kernels index chunks in 32 bits).
  * head_dim in {64, 128} (ULYS_EUNSUPPORTED otherwise).
  */
 typedef struct ulys_layout {

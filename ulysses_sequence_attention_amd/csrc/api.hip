@@ -51,6 +51,9 @@ int check_layout(const ulys_layout* L, int rank, int group) {
   if (group < -1 || group >= L->groups) return fail(ULYS_EINVAL, "group %d outside [-1, %d)", group, L->groups);
   const long long rows = (long long)L->n_rep + (long long)L->degree * L->s_local;
   if (rows > 0x7fffffffLL) return fail(ULYS_EINVAL, "joint rows %lld too large", rows);
+  // the repack kernels index 16-byte chunks of one slot in 32 bits
+  const long long chunks = (long long)L->batch * rows * (L->hq / L->degree / L->groups) * L->head_dim / 8;
+  if (chunks >= (1LL << 32)) return fail(ULYS_EINVAL, "slot of %lld 16-byte chunks exceeds 2^32", chunks);
   return ULYS_OK;
 }
 

@@ -16,7 +16,29 @@ namespace ulys {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+// Access forms and chunks per thread, chosen by measurement on MI355X (Wan
+// Ulysses-4 shapes): pack reads nontemporal and writes plainly, two chunks
+// per thread; unpack reads and writes nontemporal, two chunks per thread.
+#ifndef ULYS_PK_NTLOAD
+#define ULYS_PK_NTLOAD 1
+#endif
+#ifndef ULYS_PK_NTSTORE
+#define ULYS_PK_NTSTORE 0
+#endif
+#ifndef ULYS_UP_NTLOAD
+#define ULYS_UP_NTLOAD 1
+#endif
+#ifndef ULYS_UP_NTSTORE
+#define ULYS_UP_NTSTORE 1
+#endif
+#ifndef ULYS_PK_UNROLL
+#define ULYS_PK_UNROLL 2
+#endif
+#ifndef ULYS_UP_UNROLL
+#define ULYS_UP_UNROLL 2
+#endif
+constexpr int kPackUnroll = ULYS_PK_UNROLL;     // chunks per pack thread
+constexpr int kUnpackUnroll = ULYS_UP_UNROLL;   // chunks per unpack thread
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -51,7 +73,23 @@ __device__ __forceinline__ unsigned int e4m3_of_bf16x4(unsigned int lo, unsigned
                     bf16_to_f32(hi & 0xffffu) * inv, bf16_to_f32(hi >> 16) * inv);
 }
 
-// grid.x: 16-byte output chunks of one slot [B * rows * cpr]; grid.y = tensor * ngroups + group
+// Streaming accesses: every byte is touched once; the nontemporal forms keep
+// it from displacing cache lines other work could reuse.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load((const u32x4*)p);
+  else return *(const u32x4*)p;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(void* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, (u32x4*)p);
+  else *(u32x4*)p = v;
+}
+
+// grid.x: 16-byte output chunks of one slot [B * rows * cpr], kPackUnroll * kThreads
+// per block, thread i taking chunks i, i + kThreads, ...; grid.y = tensor * ngroups
+// + group.  All loads of a thread are issued before its stores.  Chunk indices
+// are 32-bit (the host rejects slots of 2^32 chunks or more).
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   const RepackGeom& g = a.g;
   const int tensor = blockIdx.y / g.ngroups;
@@ -60,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   const int D = g.head_dim;
   const int fp8 = a.fp8[tensor];
   const int elems_per_chunk = fp8 ? 16 : 8;       // output chunk is always 16 bytes
-  const int cpr = gh * D / elems_per_chunk;        // chunks per slot row
-  const long total = (long)g.batch * g.rows * cpr;
+  const unsigned cpr = (unsigned)(gh * D / elems_per_chunk);   // chunks per slot row
+  const unsigned total = (unsigned)g.batch * (unsigned)g.rows * cpr;
   const int H = a.heads[tensor];
   const int hbase = a.h0[tensor] + gi * gh;
   float inv = 1.0f;
@@ -71,57 +109,72 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   }
   unsigned char* dst_base = (unsigned char*)a.dst[tensor] +
                             (size_t)gi * g.batch * g.rows * gh * D * (fp8 ? 1 : 2);
-  for (int u = 0; u < kUnroll; ++u) {
-    const long idx = ((long)blockIdx.x * kUnroll + u) * kThreads + threadIdx.x;
-    if (idx >= total) break;
-    const int c = (int)(idx % cpr);
-    const long bt = idx / cpr;
-    const int t = (int)(bt % g.rows);
-    const int b = (int)(bt / g.rows);
-    int p, srow;
-    src_of_row(g, g.rank, t, &p, &srow);
-    const uint16_t* src = a.src[tensor][p] +
-                          (((size_t)b * g.shard_rows + srow) * H + hbase) * D + (size_t)c * elems_per_chunk;
-    u32x4* dst = (u32x4*)(dst_base + (size_t)idx * 16);
-    if (!fp8) {
-      *dst = *(const u32x4*)src;
-    } else {
-      const u32x4 x0 = ((const u32x4*)src)[0];
-      const u32x4 x1 = ((const u32x4*)src)[1];
-      u32x4 y;
-      y.x = e4m3_of_bf16x4(x0.x, x0.y, inv);
-      y.y = e4m3_of_bf16x4(x0.z, x0.w, inv);
-      y.z = e4m3_of_bf16x4(x1.x, x1.y, inv);
-      y.w = e4m3_of_bf16x4(x1.z, x1.w, inv);
-      *dst = y;
+  const unsigned first = blockIdx.x * (kPackUnroll * kThreads) + threadIdx.x;
+  u32x4 x0[kPackUnroll], x1[kPackUnroll];
+#pragma unroll
+  for (int u = 0; u < kPackUnroll; ++u) {
+    const unsigned idx = first + u * kThreads;
+    if (idx < total) {
+      const unsigned c = idx % cpr;
+      const unsigned bt = idx / cpr;
+      const unsigned t = bt % (unsigned)g.rows;
+      const unsigned b = bt / (unsigned)g.rows;
+      int p, srow;
+      src_of_row(g, g.rank, (int)t, &p, &srow);
+      const uint16_t* src = a.src[tensor][p] +
+                            (((size_t)b * g.shard_rows + srow) * H + hbase) * D + (size_t)c * elems_per_chunk;
+      x0[u] = ld_stream<ULYS_PK_NTLOAD>(src);
+      if (fp8) x1[u] = ld_stream<ULYS_PK_NTLOAD>(src + 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPackUnroll; ++u) {
+    const unsigned idx = first + u * kThreads;
+    if (idx < total) {
+      u32x4 y = x0[u];
+      if (fp8) {
+        y.x = e4m3_of_bf16x4(x0[u].x, x0[u].y, inv);
+        y.y = e4m3_of_bf16x4(x0[u].z, x0[u].w, inv);
+        y.z = e4m3_of_bf16x4(x1[u].x, x1[u].y, inv);
+        y.w = e4m3_of_bf16x4(x1[u].z, x1[u].w, inv);
+      }
+      st_stream<ULYS_PK_NTSTORE>(dst_base + (size_t)idx * 16, y);
     }
   }
 }
 
-// grid.x: chunks of [B * shard_rows * cpr]; grid.y = p * ngroups + group
+// grid.x: chunks of [B * shard_rows * cpr] (as pack); grid.y = p * ngroups + group
 __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a) {
   const RepackGeom& g = a.g;
   const int p = blockIdx.y / g.ngroups;
   const int gi = blockIdx.y % g.ngroups;
   const int D = g.head_dim;
-  const int cpr = a.gh * D / 8;
-  const long total = (long)g.batch * g.shard_rows * cpr;
+  const unsigned cpr = (unsigned)(a.gh * D / 8);
+  const unsigned total = (unsigned)g.batch * (unsigned)g.shard_rows * cpr;
   const int hbase = a.h0 + gi * a.gh;
   const uint16_t* src_base = a.src + (size_t)gi * g.batch * g.rows * a.gh * D;
-  for (int u = 0; u < kUnroll; ++u) {
-    const long idx = ((long)blockIdx.x * kUnroll + u) * kThreads + threadIdx.x;
-    if (idx >= total) break;
-    const int c = (int)(idx % cpr);
-    const long br = idx / cpr;
-    const int r = (int)(br % g.shard_rows);      // row within shard p
-    const int b = (int)(br / g.shard_rows);
-    int t;
-    if (g.rep_first) t = (r < g.n_rep) ? r : g.n_rep + p * g.s_local + (r - g.n_rep);
-    else t = (r < g.s_local) ? p * g.s_local + r : g.degree * g.s_local + (r - g.s_local);
-    const uint16_t* src = src_base + (((size_t)b * g.rows + t) * a.gh) * D + (size_t)c * 8;
-    uint16_t* dst = a.dst[p] + (((size_t)b * g.shard_rows + r) * a.heads + hbase) * D + (size_t)c * 8;
-    *(u32x4*)dst = *(const u32x4*)src;
+  const unsigned first = blockIdx.x * (kUnpackUnroll * kThreads) + threadIdx.x;
+  u32x4 x[kUnpackUnroll];
+  uint16_t* dst[kUnpackUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnpackUnroll; ++u) {
+    const unsigned idx = first + u * kThreads;
+    dst[u] = nullptr;
+    if (idx < total) {
+      const unsigned c = idx % cpr;
+      const unsigned br = idx / cpr;
+      const int r = (int)(br % (unsigned)g.shard_rows);      // row within shard p
+      const unsigned b = br / (unsigned)g.shard_rows;
+      int t;
+      if (g.rep_first) t = (r < g.n_rep) ? r : g.n_rep + p * g.s_local + (r - g.n_rep);
+      else t = (r < g.s_local) ? p * g.s_local + r : g.degree * g.s_local + (r - g.s_local);
+      x[u] = ld_stream<ULYS_UP_NTLOAD>(src_base + (((size_t)b * g.rows + t) * a.gh) * D + (size_t)c * 8);
+      dst[u] = a.dst[p] + (((size_t)b * g.shard_rows + r) * a.heads + hbase) * D + (size_t)c * 8;
+    }
   }
+#pragma unroll
+  for (int u = 0; u < kUnpackUnroll; ++u)
+    if (first + u * kThreads < total) st_stream<ULYS_UP_NTSTORE>(dst[u], x[u]);
 }
 
 __global__ void amax_zero_kernel(unsigned int* out) {
@@ -161,7 +214,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
     const long total = (long)a.g.batch * a.g.rows * cpr;
     if (total > most) most = total;
   }
-  const long per_block = (long)kThreads * kUnroll;
+  const long per_block = (long)kThreads * kPackUnroll;
   dim3 grid((unsigned)((most + per_block - 1) / per_block), 3 * a.g.ngroups);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -169,7 +222,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
 
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s) {
   const long total = (long)a.g.batch * a.g.shard_rows * (a.gh * a.g.head_dim / 8);
-  const long per_block = (long)kThreads * kUnroll;
+  const long per_block = (long)kThreads * kUnpackUnroll;
   dim3 grid((unsigned)((total + per_block - 1) / per_block), a.g.degree * a.g.ngroups);
   hipLaunchKernelGGL(unpack_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
