@@ -52,6 +52,13 @@ typedef enum {
   ULYS_FP8_E4M3 = 1        /* OCP e4m3fn codes, one per-tensor scale each for q and k */
 } ulys_dtype;
 
+/* ulys_layout.rep_first values */
+typedef enum {
+  ULYS_REP_SUFFIX = 0,     /* replicated rows behind the shard rows, in q, k and v */
+  ULYS_REP_PREFIX = 1,     /* replicated rows in front of the shard rows, in q, k and v */
+  ULYS_REP_KV_PREFIX = 2   /* replicated rows in front in k and v only; q and o have none */
+} ulys_rep_mode;
+
 /*
  * Layout of one Ulysses attention call, as every rank sees it.
  *
@@ -63,8 +70,16 @@ typedef enum {
  * sglang PR #43521 "Layouts" (q/k/v as [batch, s_local, heads, head_dim],
  * GQA, replicated prefix or suffix).
  *
+ * rep_first = 2 (ULYS_REP_KV_PREFIX) is cross-attention with a replicated
+ * K/V-only prefix (sglang layer.py _forward_with_replicated_kv_prefix: q is
+ * sequence-sharded with no replicated part; k/v carry the replicated prefix
+ * followed by the shard rows, which line up with q's sharding; sglang PR
+ * #43521 "Layouts", a K/V-only prefix).  Then q shards and o shards are
+ * [B, S_l, Hq, D] and k/v shards [B, R + S_l, Hkv, D]; the q and o slots
+ * hold P*S_l rows and the k/v slots R + P*S_l rows.
+ *
  * Rules (ULYS_EINVAL otherwise): batch, degree, s_local, hq, hkv, groups >= 1;
- * n_rep >= 0; rep_first in {0, 1}; P | Hq and P | Hkv (flashdreams cp.py,
+ * n_rep >= 0; rep_first in {0, 1, 2}; P | Hq and P | Hkv (flashdreams cp.py,
  * ContextParallelAttention._impl_ulysses: heads must divide by the CP size);
  * Hkv | Hq (GQA); G | Hq/P and G | Hkv/P (sglang PR #43521, "Automatic group
  * count": a group count must divide the q and k/v heads per rank); a q slot
@@ -77,7 +92,7 @@ typedef struct ulys_layout {
   int32_t degree;     /* P */
   int32_t s_local;    /* S_l */
   int32_t n_rep;      /* R, 0 = no replicated rows */
-  int32_t rep_first;  /* 1 prefix, 0 suffix */
+  int32_t rep_first;  /* ulys_rep_mode: 1 prefix, 0 suffix, 2 K/V-only prefix */
   int32_t hq;
   int32_t hkv;
   int32_t head_dim;   /* D */
@@ -100,8 +115,12 @@ typedef struct ulys_layout {
  * ranks 0..P-1], suffix [shard rows of ranks 0..P-1 | rep(r)], rep(r) being
  * shard r's copy of the replicated rows.  Groups take contiguous head blocks.
  *
+ * With a K/V-only prefix, J_r of q is the shard rows of ranks 0..P-1 alone
+ * and J_r of k/v the prefix form.
+ *
  * q_shards/k_shards/v_shards: host arrays of P device pointers (layout above).
- * q_slot: [B, rows, Gq, D], k_slot/v_slot: [B, rows, Gkv, D].  group = -1
+ * q_slot: [B, rows_q, Gq, D], k_slot/v_slot: [B, rows_kv, Gkv, D], where
+ * rows_kv = R + P*S_l and rows_q = rows_kv, or P*S_l with a K/V-only prefix.  group = -1
  * packs all G groups at once into G consecutive slots ([G][B, rows, Gh, D]).
  * q_slot and k_slot hold bf16 when qk_dtype = ULYS_BF16 and e4m3fn codes
  * (1 byte per element) when qk_dtype = ULYS_FP8_E4M3; v_slot is always bf16.
@@ -163,7 +182,7 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
  * compute_units workgroups and a partial round costs nearly a full one): G is
  * accepted when G calls take no more rounds than the one call over all the
  * rank's heads, i.e. G * ceil(W / G / cus) <= ceil(W / cus) with
- * W = batch * (Hq/P) * ceil(rows / 256).  Returns the count (>= 1; 1 = keep
+ * W = batch * (Hq/P) * ceil(rows_q / 256).  Returns the count (>= 1; 1 = keep
  * the sequential single call); layout->groups is ignored.
  * Rules: the layout rules with groups = 1; compute_units >= 1 (ULYS_EINVAL).
  */
@@ -215,6 +234,38 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       const int32_t* key_gaps, void* o, float* lse, void* stream);
 
 /*
+ * ulys_attend_group_ex -- ulys_attend_group with query and key sequences of
+ * different lengths and an optional arbitrary key mask.
+ *
+ * Source: sglang layer.py _forward_with_replicated_kv_prefix (attention of the
+ * gathered q rows over [replicated K/V prefix | gathered k/v rows]: more keys
+ * than queries); sglang PR #43521 path table, "key mask / tail padding" (a
+ * gathered key mask, attended with varlen FA or SDPA) and layer.py
+ * build_varlen_mask_meta (a [B, S] boolean key mask; masked keys take no part
+ * in any row's softmax) and LocalAttention (masked keys get zero weight).
+ *
+ * As ulys_attend_group, with q, o: [B, q_rows, hq, D], k, v: [B, kv_rows,
+ * hkv, D], lse: [B, hq, q_rows], key_gaps ranges inside [0, kv_rows], and
+ * the valid keys of batch b being those outside its gap whose bit is set in
+ * key_mask: a device array of B * ceil(kv_rows / 32) uint32 words, key j of
+ * batch b valid iff bit (j % 32) of word [b * ceil(kv_rows/32) + j / 32] is 1
+ * (bits for j >= kv_rows are ignored), or NULL for all keys valid.  Key tiles
+ * (64 keys) without a valid key are skipped.  A (b, row) left without any
+ * valid key by the mask gets o = 0 and lse = -inf (the mask is device data,
+ * so this cannot be rejected up front).  Query rows are never masked.
+ * Rules: as ulys_attend_group with q_rows, kv_rows >= 1; key_mask 4-byte
+ * aligned; with a key mask kv_rows <= 262144 (ULYS_EUNSUPPORTED otherwise).
+ * ulys_attend_group(B, rows, ...) equals ulys_attend_group_ex(B, rows, rows,
+ * ..., key_mask = NULL, ...), and a mask that marks exactly the keys outside
+ * the gaps gives the same bytes as the gaps.
+ */
+int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim,
+                         const void* q, const void* k, const void* v, int qk_dtype,
+                         float softmax_scale, const float* qk_amax,
+                         const int32_t* key_gaps, const uint32_t* key_mask,
+                         void* o, float* lse, void* stream);
+
+/*
  * ulys_unpack -- inverse of ulys_pack for the output of (rank, group).
  *
  * Source: flashdreams cp.py _impl_ulysses (output all-to-all restores the
@@ -223,8 +274,9 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  * gets it) and sglang PR #43521 "Layouts" (output returns in the caller's
  * row order).
  *
- * o_slot: [B, rows, Gq, D] bf16 (group = -1: [G][B, rows, Gq, D]).
- * o_shards: host array of P device pointers, each [B, R + S_l, Hq, D] bf16;
+ * o_slot: [B, rows_q, Gq, D] bf16 (group = -1: [G][B, rows_q, Gq, D]).
+ * o_shards: host array of P device pointers, each [B, R + S_l, Hq, D] bf16
+ * ([B, S_l, Hq, D] with a K/V-only prefix);
  * writes heads h0..h0+Gq of every shard: shard rows of rank p from their
  * joint rows, replicated rows into every shard.  Other heads are untouched.
  */
@@ -244,11 +296,11 @@ int ulys_unpack(const ulys_layout* layout, int rank, int group,
  *
  * Equivalent to, for g = 0 .. G-1 in order:
  *   ulys_pack(layout, rank, g, ...) into slot g,
- *   ulys_attend_group(B, rows, Gq, Gkv, D, slot g ..., o slot g, lse g),
+ *   ulys_attend_group_ex(B, rows_q, rows_kv, Gq, Gkv, D, slot g ..., o slot g, lse g),
  *   ulys_unpack(layout, rank, g, o slot g, o_shards)
  * and byte-identical to it.  q/k/v/o_slots hold G consecutive slots
  * ([G][B, rows, Gh, D], the group = -1 layout of ulys_pack); lse is
- * [G][B, Gq, rows] float32 or NULL.  Shards, qk_dtype, qk_amax,
+ * [G][B, Gq, rows_q] float32 or NULL.  Shards, qk_dtype, qk_amax,
  * softmax_scale and key_gaps as for ulys_pack / ulys_attend_group.
  *
  * Streams: attention runs on `stream`, packs and unpacks on `copy_stream`

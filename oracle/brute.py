@@ -10,10 +10,12 @@ from __future__ import annotations
 import math
 
 
-def attention(q, k, v, scale, key_gaps=None):
-    """q ``[B][Nq][Hq][D]``, k/v ``[B][Nk][Hkv][D]`` nested lists (or arrays).
+def attention(q, k, v, scale, key_gaps=None, key_mask=None):
+    """q ``[B][Nq][Hq][D]``, k/v ``[B][Nk][Hkv][D]`` nested lists (or arrays);
+    ``key_mask`` ``[B][Nk]`` booleans (True = valid) or None.
 
-    Returns ``(o, lse)`` as nested lists ``[B][Nq][Hq][D]`` and ``[B][Hq][Nq]``.
+    Returns ``(o, lse)`` as nested lists ``[B][Nq][Hq][D]`` and ``[B][Hq][Nq]``;
+    a batch without a valid key gets o = 0, lse = -inf.
     """
     bsz, nq, hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     nk, hkv = len(k[0]), len(k[0][0])
@@ -22,7 +24,11 @@ def attention(q, k, v, scale, key_gaps=None):
     lse = [[[0.0] * nq for _ in range(hq)] for _ in range(bsz)]
     for b in range(bsz):
         g0, g1 = (0, 0) if key_gaps is None else (int(key_gaps[b][0]), int(key_gaps[b][1]))
-        keys = [j for j in range(nk) if not (g0 <= j < g1)]
+        keys = [j for j in range(nk) if not (g0 <= j < g1) and (key_mask is None or key_mask[b][j])]
+        if not keys:
+            for h in range(hq):
+                lse[b][h] = [-math.inf] * nq
+            continue
         for h in range(hq):
             hk = h // rep
             for i in range(nq):

@@ -142,3 +142,29 @@ def unpack(o_slot: np.ndarray, out_shards: list[np.ndarray], rank: int, group: i
         else:
             out_shards[p][:, :s_local, h0:h0 + gh] = own
             out_shards[p][:, s_local:, h0:h0 + gh] = rep
+
+
+def pack_kv_prefix(q_shards: list[np.ndarray], k_shards: list[np.ndarray], v_shards: list[np.ndarray],
+                   rank: int, group: int, groups: int, n_rep: int):
+    """Receive slots of (rank, group) with a replicated K/V-only prefix.
+
+    sglang ``layer.py`` ``_forward_with_replicated_kv_prefix``: q is
+    sequence-sharded with no replicated part; k/v are ``[rep | shard]`` on
+    every rank.  Steps: all-to-all q and the k/v shard rows (seq -> head
+    shard), slice the replicated k/v prefix to the rank's heads, join it in
+    front of the gathered k/v rows.  That is the plain joint layout with no
+    replicated rows for q and the prefix layout for k/v, so the slots are
+    ``pack`` with ``n_rep = 0`` for q and ``n_rep`` in front for k and v.
+    Returns ``(q_slot [B, P*S_l, Gq, D], k_slot, v_slot [B, R + P*S_l, Gkv, D])``.
+    """
+    return (pack(q_shards, rank, group, groups, 0, True),
+            pack(k_shards, rank, group, groups, n_rep, True),
+            pack(v_shards, rank, group, groups, n_rep, True))
+
+
+def unpack_kv_prefix(o_slot: np.ndarray, out_shards: list[np.ndarray], rank: int, group: int,
+                     groups: int) -> None:
+    """Inverse of the q permutation of ``pack_kv_prefix`` for the output: the
+    output carries no replicated rows (``_usp_output_all_to_all`` of the
+    attention output alone), so it is ``unpack`` with ``n_rep = 0``."""
+    unpack(o_slot, out_shards, rank, group, groups, 0, True)

@@ -28,8 +28,8 @@ def _declared():
 
 def test_header_declares_the_path():
     names = _declared()
-    for n in ("ulys_pack", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
-              "ulys_auto_groups", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
+    for n in ("ulys_pack", "ulys_attend_group", "ulys_attend_group_ex", "ulys_unpack", "ulys_rank_pipeline",
+              "ulys_lse_merge", "ulys_auto_groups", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
         assert n in names
 
 
@@ -88,7 +88,7 @@ def test_pack_rules(U):
     assert _pack(U, GOOD, slots=(FAKE, None, FAKE)) == -1
     assert _pack(U, GOOD, slots=(FAKE, FAKE, MIS)) == -1
     c = U.Layout(**GOOD).c_struct()
-    c.rep_first = 2
+    c.rep_first = 3                                                     # modes are 0, 1, 2
     assert _pack(U, c) == -1
     assert U.call_raw("ulys_pack", None, 0, 0, _arr(4), _arr(4), _arr(4), FAKE, FAKE, FAKE, 0, None, None) == -1
     assert "layout" in U.last_error()
@@ -120,6 +120,26 @@ def test_attend_rules(U):
     assert "no valid key" in U.last_error()
     assert _attend(U, batch=2, gaps=[0, 10, 0, 100]) == -1
     assert _attend(U, batch=300, gaps=[0, 1] * 300) == -1             # too many gap batches
+
+
+def _attend_ex(U, batch=1, nq=100, nk=140, hq=2, hkv=2, d=128, dtype=0, gaps=None, mask=None):
+    g = None
+    if gaps is not None:
+        g = (ctypes.c_int32 * len(gaps))(*gaps)
+    return U.call_raw("ulys_attend_group_ex", batch, nq, nk, hq, hkv, d, FAKE, FAKE, FAKE, dtype, ctypes.c_float(0.0),
+                      None, g, mask, FAKE, None, None)
+
+
+def test_attend_ex_rules(U):
+    assert _attend_ex(U, nq=0) == -1
+    assert _attend_ex(U, nk=0) == -1
+    assert _attend_ex(U, hq=3, hkv=2) == -1
+    assert _attend_ex(U, d=96) == -2
+    assert _attend_ex(U, gaps=[120, 141]) == -1                        # gaps are on keys: past nk = 140
+    assert _attend_ex(U, gaps=[0, 140]) == -1                          # no valid key
+    assert _attend_ex(U, mask=FAKE + 2) == -1                          # mask words 4-byte aligned
+    assert _attend_ex(U, nk=262144 + 64, mask=FAKE) == -2              # key-mask tile list limit
+    assert "key mask" in U.last_error()
 
 
 def test_unpack_and_amax_rules(U):
@@ -222,3 +242,17 @@ def test_binding_refuses_cpu_tensors(U):
     x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         U.ulys_attend_group(x, x, x, x)
+
+
+def test_key_mask_word_encoding():
+    """inputs.key_mask_words follows the header's encoding: key j of batch b valid iff bit j % 32 of
+    word [b][j // 32] is set (checked bit by bit)."""
+    import numpy as np
+    from ulysses_sequence_attention_amd import inputs
+    m = inputs.random_key_mask(3, 100, 5, 0.5)
+    w = inputs.key_mask_words(m).numpy().view(np.uint32)
+    assert w.shape == (3, 4)
+    for b in range(3):
+        for j in range(128):
+            bit = (int(w[b, j // 32]) >> (j % 32)) & 1
+            assert bit == (int(m[b, j]) if j < 100 else 0)

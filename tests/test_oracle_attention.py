@@ -168,3 +168,84 @@ def test_errors():
         oa.attention(q, q, q, 1.0, [(3, 5)])      # gap out of range
     with pytest.raises(ValueError):
         oa.attention(np.zeros((1, 4, 3, 2)), q.repeat(2, axis=2), q.repeat(2, axis=2), 1.0)
+
+
+def _sdpa_mask_ref(q, k, v, scale, key_mask):
+    """torch float64 SDPA with an arbitrary [B, Nk] boolean key mask (broadcast over heads and rows)."""
+    qt = torch.from_numpy(q).transpose(1, 2)
+    kt = torch.from_numpy(k).transpose(1, 2)
+    vt = torch.from_numpy(v).transpose(1, 2)
+    rep = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(rep, dim=1)
+    vt = vt.repeat_interleave(rep, dim=1)
+    mask = torch.from_numpy(key_mask)[:, None, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return out.transpose(1, 2).numpy()
+
+
+def _rand_mask(b, nk, seed, p=0.5):
+    m = np.random.default_rng(seed).random((b, nk)) < p
+    m[:, 0] = True            # every batch keeps a valid key
+    return m
+
+
+@pytest.mark.parametrize("b,nq,nk,hq,hkv,d", [(1, 7, 12, 2, 2, 8), (2, 9, 5, 4, 2, 4), (2, 6, 11, 3, 1, 6)])
+def test_mask_matches_bruteforce(b, nq, nk, hq, hkv, d):
+    """Arbitrary key masks and Nq != Nk against exactly rounded loops."""
+    q, k, v = _rand((b, nq, hq, d), 11), _rand((b, nk, hkv, d), 12), _rand((b, nk, hkv, d), 13)
+    m = _rand_mask(b, nk, 5)
+    o, lse = oa.attention(q, k, v, 0.41, key_mask=m, block=3)
+    ob, lseb = brute.attention(q.tolist(), k.tolist(), v.tolist(), float(np.float32(0.41)), key_mask=m.tolist())
+    assert np.max(np.abs(o - np.array(ob))) < 1e-12
+    assert np.max(np.abs(lse - np.array(lseb))) < 1e-12
+
+
+@pytest.mark.parametrize("b,nq,nk,hq,hkv,d,p", [(1, 40, 90, 4, 4, 16, 0.3), (2, 64, 64, 8, 2, 32, 0.8),
+                                               (1, 33, 130, 2, 1, 8, 0.05)])
+def test_mask_matches_sdpa(b, nq, nk, hq, hkv, d, p):
+    q, k, v = _rand((b, nq, hq, d), 21), _rand((b, nk, hkv, d), 22), _rand((b, nk, hkv, d), 23)
+    m = _rand_mask(b, nk, 7, p)
+    scale = oa.default_scale(d)
+    o, _ = oa.attention(q, k, v, scale, key_mask=m)
+    assert np.max(np.abs(o - _sdpa_mask_ref(q, k, v, scale, m))) < 1e-12
+
+
+def test_mask_of_gap_equals_gap_and_combines():
+    """A mask marking the keys outside a gap is the gap; gap and mask together keep their intersection."""
+    b, n, h, d = 2, 50, 2, 8
+    q, k, v = _rand((b, n, h, d), 31), _rand((b, n, h, d), 32), _rand((b, n, h, d), 33)
+    gaps = [(10, 30), (0, 17)]
+    m = np.ones((b, n), dtype=bool)
+    for i, (g0, g1) in enumerate(gaps):
+        m[i, g0:g1] = False
+    o1, l1 = oa.attention(q, k, v, 0.3, gaps)
+    o2, l2 = oa.attention(q, k, v, 0.3, key_mask=m)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    m2 = _rand_mask(b, n, 9)
+    o3, _ = oa.attention(q, k, v, 0.3, gaps, key_mask=m2)
+    o4, _ = oa.attention(q, k, v, 0.3, key_mask=m & m2)
+    assert np.array_equal(o3, o4)
+
+
+def test_masked_kv_contents_do_not_matter():
+    b, nq, nk, h, d = 1, 20, 45, 2, 8
+    q, k, v = _rand((b, nq, h, d), 41), _rand((b, nk, h, d), 42), _rand((b, nk, h, d), 43)
+    m = _rand_mask(b, nk, 11)
+    o1, l1 = oa.attention(q, k, v, 0.5, key_mask=m)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, ~m[0]] = 1e4
+    v2[:, ~m[0]] = -1e4
+    o2, l2 = oa.attention(q, k2, v2, 0.5, key_mask=m)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_all_masked_batch_gives_zero_and_neg_inf():
+    b, n, h, d = 2, 10, 2, 4
+    q, k, v = _rand((b, n, h, d), 51), _rand((b, n, h, d), 52), _rand((b, n, h, d), 53)
+    m = np.ones((b, n), dtype=bool)
+    m[1] = False
+    o, lse = oa.attention(q, k, v, 0.5, key_mask=m)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    ob, lseb = brute.attention(q.tolist(), k.tolist(), v.tolist(), 0.5, key_mask=m.tolist())
+    assert np.all(np.array(ob)[1] == 0) and np.all(np.isneginf(np.array(lseb)[1]))
+    assert np.all(np.isfinite(lse[0]))

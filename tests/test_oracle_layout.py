@@ -181,3 +181,48 @@ def test_divisibility_errors():
         layout.group_heads(10, 4, 1)
     with pytest.raises(ValueError):
         layout.group_heads(8, 4, 3)
+
+
+def _sglang_kv_prefix_inputs(q_shards, k_shards, v_shards, rank, n_rep):
+    """_forward_with_replicated_kv_prefix_split for rank: all-to-all q and the k/v shard
+    rows, slice the replicated k/v prefix to the rank's k/v heads, join it in front."""
+    q = _sglang_a2a_in(q_shards, rank)
+    k_sh = _sglang_a2a_in([s[:, n_rep:] for s in k_shards], rank)
+    v_sh = _sglang_a2a_in([s[:, n_rep:] for s in v_shards], rank)
+    h_kv_local = k_sh.shape[2]
+    h0 = rank * h_kv_local
+    k_rep = k_shards[rank][:, :n_rep, h0:h0 + h_kv_local]
+    v_rep = v_shards[rank][:, :n_rep, h0:h0 + h_kv_local]
+    return q, torch.cat([k_rep, k_sh], dim=1), torch.cat([v_rep, v_sh], dim=1)
+
+
+@pytest.mark.parametrize("w,b,s_l,n_rep,hq,hkv,d", [(2, 1, 5, 3, 4, 4, 8), (4, 2, 3, 6, 8, 4, 4), (4, 1, 2, 1, 4, 4, 2)])
+def test_pack_kv_prefix_matches_sglang_steps(w, b, s_l, n_rep, hq, hkv, d):
+    """K/V-only prefix: q has no replicated rows; k/v = [rep sliced to the rank's heads | gathered rows]."""
+    q_shards = [_rand((b, s_l, hq, d), 10 + p) for p in range(w)]
+    k_shards = [_rand((b, n_rep + s_l, hkv, d), 20 + p) for p in range(w)]
+    v_shards = [_rand((b, n_rep + s_l, hkv, d), 30 + p) for p in range(w)]
+    # every rank holds the same replicated k/v prefix
+    for lst in (k_shards, v_shards):
+        for p in range(1, w):
+            lst[p][:, :n_rep] = lst[0][:, :n_rep]
+    for r in range(w):
+        q_ref, k_ref, v_ref = _sglang_kv_prefix_inputs(q_shards, k_shards, v_shards, r, n_rep)
+        qs, ks, vs = layout.pack_kv_prefix([x.float().numpy() for x in q_shards], [x.float().numpy() for x in k_shards],
+                                           [x.float().numpy() for x in v_shards], r, 0, 1, n_rep)
+        assert np.array_equal(qs, q_ref.float().numpy())
+        assert np.array_equal(ks, k_ref.float().numpy())
+        assert np.array_equal(vs, v_ref.float().numpy())
+
+
+def test_unpack_kv_prefix_restores_q_shards():
+    """Round trip: unpacking a copy of every rank's q slot (every group) gives the q shards back."""
+    w, b, s_l, h, d, groups = 4, 2, 3, 8, 4, 2
+    q_shards = [_rand((b, s_l, h, d), 40 + p).float().numpy() for p in range(w)]
+    out = [np.zeros_like(x) for x in q_shards]
+    for r in range(w):
+        for g in range(groups):
+            qs = layout.pack(q_shards, r, g, groups, 0, True)
+            layout.unpack_kv_prefix(qs.copy(), out, r, g, groups)
+    for p in range(w):
+        assert np.array_equal(out[p], q_shards[p])

@@ -37,7 +37,7 @@ int check_layout(const ulys_layout* L, int rank, int group) {
   if (L->batch < 1 || L->degree < 1 || L->s_local < 1 || L->hq < 1 || L->hkv < 1 || L->groups < 1)
     return fail(ULYS_EINVAL, "batch, degree, s_local, hq, hkv and groups must be >= 1");
   if (L->n_rep < 0) return fail(ULYS_EINVAL, "n_rep must be >= 0");
-  if (L->rep_first != 0 && L->rep_first != 1) return fail(ULYS_EINVAL, "rep_first must be 0 or 1");
+  if (L->rep_first < 0 || L->rep_first > 2) return fail(ULYS_EINVAL, "rep_first must be 0, 1 or 2");
   if (L->degree > ulys::kMaxDegree) return fail(ULYS_EINVAL, "degree %d exceeds %d", L->degree, ulys::kMaxDegree);
   if (L->hq % L->degree || L->hkv % L->degree)
     return fail(ULYS_EINVAL, "heads (hq %d, hkv %d) must divide by the Ulysses degree %d", L->hq, L->hkv, L->degree);
@@ -52,7 +52,8 @@ int check_layout(const ulys_layout* L, int rank, int group) {
   const long long rows = (long long)L->n_rep + (long long)L->degree * L->s_local;
   if (rows > 0x7fffffffLL) return fail(ULYS_EINVAL, "joint rows %lld too large", rows);
   // the repack kernels index 16-byte chunks of one slot in 32 bits
-  const long long chunks = (long long)L->batch * rows * (L->hq / L->degree / L->groups) * L->head_dim / 8;
+  const long long hmax = L->hq > L->hkv ? L->hq : L->hkv;
+  const long long chunks = (long long)L->batch * rows * (hmax / L->degree / L->groups) * L->head_dim / 8;
   if (chunks >= (1LL << 32)) return fail(ULYS_EINVAL, "slot of %lld 16-byte chunks exceeds 2^32", chunks);
   return ULYS_OK;
 }
@@ -72,16 +73,20 @@ int check_ptr(const void* p, const char* what) {
   return ULYS_OK;
 }
 
-ulys::RepackGeom geom_of(const ulys_layout* L, int rank, int group) {
+// Repack geometry of one tensor: q (and the output o) or k/v.  With a K/V-only
+// prefix (rep_first = 2) q and o carry no replicated rows and k/v carry them
+// in front, as with a prefix.
+ulys::RepackGeom geom_of(const ulys_layout* L, int rank, int group, bool is_q) {
   ulys::RepackGeom g;
+  const int n_rep = (L->rep_first == ULYS_REP_KV_PREFIX && is_q) ? 0 : L->n_rep;
   g.batch = L->batch;
   g.degree = L->degree;
   g.s_local = L->s_local;
-  g.n_rep = L->n_rep;
-  g.rep_first = L->rep_first;
+  g.n_rep = n_rep;
+  g.rep_first = L->rep_first == 0 ? 0 : 1;
   g.rank = rank;
-  g.rows = L->n_rep + L->degree * L->s_local;
-  g.shard_rows = L->n_rep + L->s_local;
+  g.rows = n_rep + L->degree * L->s_local;
+  g.shard_rows = n_rep + L->s_local;
   g.head_dim = L->head_dim;
   g.ngroups = group < 0 ? L->groups : 1;
   return g;
@@ -118,7 +123,7 @@ int prepare_pack(const ulys_layout* L, int rank, int group, const void* const* q
   if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
 
   memset(&a, 0, sizeof a);
-  a.g = geom_of(L, rank, group);
+  for (int t = 0; t < 3; ++t) a.g[t] = geom_of(L, rank, group, t == 0);
   const int heads[3] = {L->hq, L->hkv, L->hkv};
   const void* const* src[3] = {q_shards, k_shards, v_shards};
   void* dst[3] = {q_slot, k_slot, v_slot};
@@ -136,16 +141,17 @@ int prepare_pack(const ulys_layout* L, int rank, int group, const void* const* q
 }
 
 // Validated launch arguments of an attention call; nothing is enqueued.
-int prepare_attend(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
+int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim, const void* q, const void* k,
                    const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
-                   const int32_t* key_gaps, void* o, float* lse, ulys::AttnArgs& a) {
-  if (batch < 1 || rows < 1 || hq < 1 || hkv < 1)
-    return fail(ULYS_EINVAL, "batch, rows, hq and hkv must be >= 1");
+                   const int32_t* key_gaps, const uint32_t* key_mask, void* o, float* lse, ulys::AttnArgs& a) {
+  if (batch < 1 || q_rows < 1 || kv_rows < 1 || hq < 1 || hkv < 1)
+    return fail(ULYS_EINVAL, "batch, q_rows, kv_rows, hq and hkv must be >= 1");
   if (hq % hkv) return fail(ULYS_EINVAL, "hq %d must be a multiple of hkv %d", hq, hkv);
   if (head_dim != 64 && head_dim != 128) return fail(ULYS_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
   if (qk_dtype != ULYS_BF16 && qk_dtype != ULYS_FP8_E4M3) return fail(ULYS_EINVAL, "qk_dtype %d unknown", qk_dtype);
   if (batch > 65535 || hq > 65535) return fail(ULYS_EINVAL, "batch and hq must be <= 65535");
-  if ((long long)batch * rows * hq * head_dim > (1LL << 40)) return fail(ULYS_EINVAL, "tensor too large");
+  if ((long long)batch * q_rows * hq * head_dim > (1LL << 40) || (long long)batch * kv_rows * hkv * head_dim > (1LL << 40))
+    return fail(ULYS_EINVAL, "tensor too large");
   int st;
   if ((st = check_ptr(q, "q"))) return st;
   if ((st = check_ptr(k, "k"))) return st;
@@ -157,15 +163,22 @@ int prepare_attend(int batch, int rows, int hq, int hkv, int head_dim, const voi
   if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(ULYS_EINVAL, "softmax_scale must be finite");
+  if (key_mask != nullptr) {
+    if ((uintptr_t)key_mask & 3u) return fail(ULYS_EINVAL, "key_mask is not 4-byte aligned");
+    const long long tiles = ((long long)kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile;
+    if (tiles > ulys::kMaxMaskTiles)
+      return fail(ULYS_EUNSUPPORTED, "a key mask over %d keys exceeds %d", kv_rows,
+                  ulys::kMaxMaskTiles * ulys::kAttnKeysPerTile);
+  }
 
   memset(&a, 0, sizeof a);
   if (key_gaps != nullptr) {
     if (batch > ulys::kMaxGapBatch) return fail(ULYS_EINVAL, "key gaps for batch %d > %d", batch, ulys::kMaxGapBatch);
     for (int b = 0; b < batch; ++b) {
       const int g0 = key_gaps[2 * b], g1 = key_gaps[2 * b + 1];
-      if (g0 < 0 || g1 < g0 || g1 > rows)
-        return fail(ULYS_EINVAL, "key gap [%d, %d) of batch %d outside [0, %d]", g0, g1, b, rows);
-      if (g1 - g0 >= rows) return fail(ULYS_EINVAL, "batch %d has no valid key", b);
+      if (g0 < 0 || g1 < g0 || g1 > kv_rows)
+        return fail(ULYS_EINVAL, "key gap [%d, %d) of batch %d outside [0, %d]", g0, g1, b, kv_rows);
+      if (g1 - g0 >= kv_rows) return fail(ULYS_EINVAL, "batch %d has no valid key", b);
       a.gap[b][0] = g0;
       a.gap[b][1] = g1;
     }
@@ -179,9 +192,12 @@ int prepare_attend(int batch, int rows, int hq, int hkv, int head_dim, const voi
   a.amax = qk_amax;
   a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
   a.batch = batch;
-  a.rows = rows;
+  a.q_rows = q_rows;
+  a.kv_rows = kv_rows;
   a.hq = hq;
   a.hkv = hkv;
+  a.key_mask = key_mask;
+  a.mask_words = (kv_rows + 31) / 32;
   return ULYS_OK;
 }
 
@@ -193,7 +209,7 @@ int prepare_unpack(const ulys_layout* L, int rank, int group, const void* o_slot
   if ((st = check_ptr(o_slot, "o_slot"))) return st;
   if ((st = check_ptr_array((const void* const*)o_shards, L->degree, "o_shards"))) return st;
   memset(&a, 0, sizeof a);
-  a.g = geom_of(L, rank, group);
+  a.g = geom_of(L, rank, group, true);
   a.src = (const uint16_t*)o_slot;
   for (int p = 0; p < L->degree; ++p) a.dst[p] = (uint16_t*)o_shards[p];
   a.heads = L->hq;
@@ -237,8 +253,18 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const 
                       const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
                       const int32_t* key_gaps, void* o, float* lse, void* stream) {
   ulys::AttnArgs a;
-  const int st = prepare_attend(batch, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax, key_gaps,
-                                o, lse, a);
+  const int st = prepare_attend(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax,
+                                key_gaps, nullptr, o, lse, a);
+  if (st) return st;
+  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
+}
+
+int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim, const void* q,
+                         const void* k, const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
+                         const int32_t* key_gaps, const uint32_t* key_mask, void* o, float* lse, void* stream) {
+  ulys::AttnArgs a;
+  const int st = prepare_attend(batch, q_rows, kv_rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale,
+                                qk_amax, key_gaps, key_mask, o, lse, a);
   if (st) return st;
   return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
 }
@@ -261,18 +287,18 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
   ulys::UnpackArgs up;
   if ((st = prepare_unpack(L, rank, -1, o_slots, o_shards, up))) return st;
   const int G = L->groups;
-  const int rows = pk.g.rows;
+  const int q_rows = pk.g[0].rows, kv_rows = pk.g[1].rows;
   const int gq = L->hq / L->degree / G, gkv = L->hkv / L->degree / G;
   ulys::AttnArgs at;
-  if ((st = prepare_attend(L->batch, rows, gq, gkv, L->head_dim, q_slots, k_slots, v_slots, qk_dtype, softmax_scale,
-                           qk_amax, key_gaps, o_slots, lse, at)))
+  if ((st = prepare_attend(L->batch, q_rows, kv_rows, gq, gkv, L->head_dim, q_slots, k_slots, v_slots, qk_dtype,
+                           softmax_scale, qk_amax, key_gaps, nullptr, o_slots, lse, at)))
     return st;
   if (G > ulys::kMaxPipelineGroups)
     return fail(ULYS_EUNSUPPORTED, "pipeline of %d groups exceeds %d", G, ulys::kMaxPipelineGroups);
   const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
   const size_t qk_elem = fp8 ? 1 : 2;
-  const size_t elems_q = (size_t)L->batch * rows * gq * L->head_dim;
-  const size_t elems_kv = (size_t)L->batch * rows * gkv * L->head_dim;
+  const size_t elems_q = (size_t)L->batch * q_rows * gq * L->head_dim;
+  const size_t elems_kv = (size_t)L->batch * kv_rows * gkv * L->head_dim;
   hipStream_t cs = (hipStream_t)stream, xs = (hipStream_t)copy_stream;
 
   // Events: start (compute -> copy), pack(g) (copy -> compute), attend(g)
@@ -294,7 +320,7 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
 
   auto pack_g = [&](int g) {
     ulys::PackArgs a = pk;
-    a.g.ngroups = 1;
+    for (int t = 0; t < 3; ++t) a.g[t].ngroups = 1;
     for (int t = 0; t < 3; ++t) {
       const size_t bytes = (t == 0 ? elems_q : elems_kv) * (t < 2 ? qk_elem : 2);
       a.dst[t] = (unsigned char*)pk.dst[t] + (size_t)g * bytes;
@@ -308,7 +334,7 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
     a.k = (const unsigned char*)k_slots + (size_t)g * elems_kv * qk_elem;
     a.v = (const unsigned char*)v_slots + (size_t)g * elems_kv * 2;
     a.o = (uint16_t*)o_slots + (size_t)g * elems_q;
-    a.lse = lse == nullptr ? nullptr : lse + (size_t)g * L->batch * gq * rows;
+    a.lse = lse == nullptr ? nullptr : lse + (size_t)g * L->batch * gq * q_rows;
     return ulys::launch_attn(a, L->head_dim, fp8, cs);
   };
   auto unpack_g = [&](int g) {
@@ -387,7 +413,9 @@ int ulys_auto_groups(const ulys_layout* L, int compute_units) {
   one.groups = 1;
   const int st = check_layout(&one, 0, -1);
   if (st) return st;
-  const long long rows = (long long)L->n_rep + (long long)L->degree * L->s_local;
+  // query rows of one call (a K/V-only prefix adds keys, not query rows)
+  const long long rows = (L->rep_first == ULYS_REP_KV_PREFIX ? 0LL : (long long)L->n_rep) +
+                         (long long)L->degree * L->s_local;
   const long long hq_rank = L->hq / L->degree, hkv_rank = L->hkv / L->degree;
   // Workgroups of the one-call attention (256 query rows each, one per CU at
   // a time) and the rounds of CUs they take.

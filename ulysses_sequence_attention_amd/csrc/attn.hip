@@ -57,24 +57,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-#ifndef ULYS_ATTN_XCD
-#define ULYS_ATTN_XCD 0
-#endif
-#ifndef ULYS_ATTN_UNROLL
-#define ULYS_ATTN_UNROLL 0
-#endif
-#ifndef ULYS_ATTN_STAGES
-#define ULYS_ATTN_STAGES 3
-#endif
-
-#ifndef ULYS_ATTN_WAVES
-#define ULYS_ATTN_WAVES 8
-#endif
-constexpr int kWaves = ULYS_ATTN_WAVES;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;             // query rows per workgroup
-constexpr int kBN = 64;                      // keys per LDS tile (two 32-key blocks)
-constexpr int kStages = ULYS_ATTN_STAGES;     // LDS ring depth (tiles)
+constexpr int kBN = kAttnKeysPerTile;        // keys per LDS tile (two 32-key blocks)
+constexpr int kStages = 3;                   // LDS ring depth (tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
@@ -135,7 +122,7 @@ __device__ __forceinline__ unsigned int lds_u32(const void* p) {
   return (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, FP8>;
@@ -144,6 +131,8 @@ void attn_fwd_kernel(AttnArgs a) {
   // does not wait for in-flight tile loads before every LDS read.
   // The LDS ring: three stages of one K tile and one V tile each.
   __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * (C::kKTile + C::kVTile)];
+  // Tiles with at least one valid key, in order, when a key mask is given.
+  __shared__ unsigned short tile_list[kMaxMaskTiles];
   // Stage st's K tile; its V tile sits at v_of(st) + the V region offset, which
   // the per-lane V read offsets carry (so every LDS read's immediate offset
   // stays below 64 KB).
@@ -157,27 +146,11 @@ void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-#if ULYS_ATTN_XCD
-  // Workgroups are dealt to the 8 XCDs round robin (id % 8); give each XCD a
-  // contiguous run of (batch, head, query tile) so the workgroups sharing an
-  // XCD's L2 stream the same head's K/V.
-  int qtile, head, b;
-  {
-    const int nq = (a.rows + kBM - 1) / kBM;
-    const int total = nq * a.hq * a.batch;
-    const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
-    const int per = total >> 3, rem = total & 7;
-    const int n = xcd * per + min(xcd, rem) + j;
-    qtile = n % nq;
-    head = (n / nq) % a.hq;
-    b = n / (nq * a.hq);
-  }
-#else
   const int qtile = blockIdx.x;
   const int head = blockIdx.y;
   const int b = blockIdx.z;
-#endif
-  const int rows = a.rows;
+  const int qrows = a.q_rows;
+  const int rows = a.kv_rows;   // keys
   const int kvh = head / (a.hq / a.hkv);
 
   float c = a.scale;
@@ -205,14 +178,14 @@ void attn_fwd_kernel(AttnArgs a) {
   {
     const int row = qrow0 + l32;
     const unsigned char* qp = (const unsigned char*)a.q +
-        (((size_t)b * rows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
+        (((size_t)b * qrows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
 #pragma unroll
     for (int kk = 0; kk < C::kQKSteps; ++kk) {
       const int off = FP8 ? (kk * 64 + hh * 32) : (kk * 16 + hh * 8) * 2;   // bytes
 #pragma unroll
       for (int part = 0; part < kQRegs / 4; ++part) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < rows) x = ld16(qp + off + part * 16);
+        if (row < qrows) x = ld16(qp + off + part * 16);
         qf[kk][part * 4 + 0] = x.x; qf[kk][part * 4 + 1] = x.y;
         qf[kk][part * 4 + 2] = x.z; qf[kk][part * 4 + 3] = x.w;
       }
@@ -369,17 +342,40 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int e = 0; e < 2; ++e) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.x[db][e], p[e], o[db], 0, 0, 0);
   };
 
-  // Tail keys and keys inside the gap -> -inf: branch-free selects under one
-  // wave-uniform branch (the key of register r is kb0 + 8 (r/4) + 4 hh + r%4).
-  auto mask = [&](f32x16& s, int kb0) ULYS_INLINE {
-    if (kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs)) {
-      const int kl = kb0 + 4 * hh;
+  // Valid-key bits of the 32 keys from kb0 (bit j: key kb0 + j): inside
+  // [0, rows), outside the gap, and set in the key mask when one is given.
+  // (MASK: the launch was given a key mask; without one, none of the mask code is compiled in)
+  const uint32_t* mask_row = MASK ? a.key_mask + (size_t)b * a.mask_words : nullptr;
+  auto bits_in = [](int k0, int lo, int hi) -> unsigned {
+    const int x = min(max(lo - k0, 0), 32), y = min(max(hi - k0, 0), 32);
+    if (y <= x) return 0u;
+    const unsigned below_y = y == 32 ? ~0u : ((1u << y) - 1u);
+    const unsigned below_x = x == 32 ? ~0u : ((1u << x) - 1u);
+    return below_y & ~below_x;
+  };
+  auto mask_word = [&](int kb0) -> unsigned {   // a load issued a block ahead of its use, or all valid
+    if constexpr (MASK) return kb0 < rows ? mask_row[kb0 >> 5] : 0u;
+    else return ~0u;
+  };
+  auto straddles = [&](int kb0) { return kb0 + 32 > rows || (kb0 < ge && kb0 + 32 > gs); };
+  auto valid_bits = [&](int kb0, unsigned mword) -> unsigned {
+    unsigned v = mword;
+    if (straddles(kb0)) v &= bits_in(kb0, 0, rows) & ~bits_in(kb0, gs, ge);
+    return v;
+  };
+
+  // Invalid keys of the block from kb0 -> -inf: selects under one wave-uniform
+  // branch, taken for blocks that straddle the end or the gap, or whose mask
+  // word (uniform, scalar) is not all ones (the key of register r is
+  // kb0 + 8 (r/4) + 4 hh + r%4).
+  auto mask = [&](f32x16& s, int kb0, unsigned mword) ULYS_INLINE {
+    if (straddles(kb0) || (MASK && mword != ~0u)) {
+      const unsigned vbits = __builtin_amdgcn_readfirstlane(valid_bits(kb0, mword));
+      // (volatile: keeps this lane-dependent work inside the rarely taken branch)
+      unsigned lb;
+      asm volatile("v_lshrrev_b32 %0, %1, %2" : "=v"(lb) : "v"(4 * hh), "s"(vbits));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kidx = kl + 8 * (r >> 2) + (r & 3);
-        const bool dead = (kidx >= rows) | ((kidx >= gs) & (kidx < ge));
-        s[r] = dead ? -INFINITY : s[r];
-      }
+      for (int r = 0; r < 16; ++r) s[r] = ((lb >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
     }
   };
 
@@ -422,8 +418,8 @@ void attn_fwd_kernel(AttnArgs a) {
   // previous block were formed with the old max and are already accumulated,
   // so O and l are rescaled by exp2(m_old - m_new); then this block's scores
   // are recomputed from K in LDS and its probabilities redone with the new max.
-  auto raise_max = [&](float pm, const unsigned char* kl, int kb, int kb0, bf16x8 (&p)[2], float& ls0,
-                       float& ls1) ULYS_INLINE {
+  auto raise_max = [&](float pm, const unsigned char* kl, int kb, int kb0, unsigned mword, bf16x8 (&p)[2],
+                       float& ls0, float& ls1) ULYS_INLINE {
     const float mx = lane_swap_max(pm) * c2;
     const float mn = fmaxf(m_run, mx);
     const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -438,7 +434,7 @@ void attn_fwd_kernel(AttnArgs a) {
     KFrag kf;
     read_k(kl, kb, kf);
     f32x16 s = qk(kf);
-    mask(s, kb0);
+    mask(s, kb0, mword);
     probs(s, p, ls0, ls1);
   };
 
@@ -478,10 +474,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Block b: s_in = S(b), p_in = P(b-1), vf = V(b-1) operands.  Produces
   // s_out = S(b+1) (K of stage st_next, block kb_next), p_out = P(b), and
-  // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b.
-  auto iteration = [&](auto st_next, auto kb_next, auto st, auto kb, int kb0, f32x16& s_in, f32x16& s_out,
-                       bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
-    mask(s_in, kb0);
+  // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b,
+  // mword = its key-mask word.
+  auto iteration = [&](auto st_next, auto kb_next, auto st, auto kb, int kb0, unsigned mword, f32x16& s_in,
+                       f32x16& s_out, bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
+    mask(s_in, kb0, mword);
     // phase 1: K reads of block b+1; PV(b-1) MFMAs under the row max and the
     // first half of the probabilities of block b
     KFrag kf;
@@ -502,77 +499,103 @@ void attn_fwd_kernel(AttnArgs a) {
                std::integral_constant<int, (kVReads + kQKMfma - 1) / kQKMfma>{},
                std::integral_constant<int, (29 + kQKMfma - 1) / kQKMfma>{});
     pin(p_out, ls0, ls1);
-    if (__any(pm > thr)) raise_max(pm, k_of(st), kb, kb0, p_out, ls0, ls1);
+    if (__any(pm > thr)) raise_max(pm, k_of(st), kb, kb0, mword, p_out, ls0, ls1);
     l_run += ls0 + ls1;
   };
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  // Tiles in processing order: all tiles except those wholly inside the gap.
+  // Tiles in processing order: every tile with a valid key.  Without a key
+  // mask these are all tiles except those wholly inside the gap; with one,
+  // the workgroup lists them in LDS first (each thread tests a run of tiles,
+  // then an exclusive scan of the counts places them).
   const int nskip = max(0, skip_last - skip_first);
-  const int nseq = ntiles - nskip;
-  auto seq_tile = [&](int pos) { return pos < skip_first ? pos : pos + nskip; };
+  int nseq = ntiles - nskip;
+  if constexpr (MASK) {
+    const int per = (ntiles + kThreads - 1) / kThreads;
+    const int t0 = min(tid * per, ntiles), t1 = min(t0 + per, ntiles);
+    int cnt = 0;
+    for (int t = t0; t < t1; ++t)   // (each thread its own tiles: lane-local bits)
+      cnt += (valid_bits(t * kBN, mask_word(t * kBN)) | valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) != 0u;
+    int* scan = (int*)lds;   // the ring is not in use yet
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    int pos = scan[tid] - cnt;
+    nseq = scan[kThreads - 1];
+    for (int t = t0; t < t1; ++t)
+      if ((valid_bits(t * kBN, mask_word(t * kBN)) | valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) != 0u)
+        tile_list[pos++] = (unsigned short)t;
+    __syncthreads();
+  }
+  // (uniform across the workgroup: kept in scalar registers)
+  auto seq_tile = [&](int pos) {
+    if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
+    else return pos < skip_first ? pos : pos + nskip;
+  };
   // Position pos goes to stage pos % kStages; past the end the last tile is
   // loaded again, which keeps every wave's load count per tile uniform.
   auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, nseq - 1)), st); };
 
-  load_pos(0, std::integral_constant<int, 0>{});
-  load_pos(1, std::integral_constant<int, 1>{});
-  if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  {
-    KFrag kf;
-    read_k(k_of(B0{}), B0{}, kf);
-    sA = qk(kf);
-    read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
-  }
-  int tc = seq_tile(0);
-  iteration(B0{}, B1{}, B0{}, B0{}, tc * kBN, sA, sB, pA, pB);
-  tile_barrier();
-
-  // Position i (stage SA): its second block, then the first block of
-  // position i+1 (stage SB).  Position i + kStages - 1 is loaded first, into
-  // SP, the stage of position i-1, which every wave has finished with.  Each
-  // step ends with a barrier.  Returns false after the last position.
-  auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
-    load_pos(i + kStages - 1, SP);
-    iteration(SB, B0{}, SA, B1{}, tc * kBN + 32, sB, sA, pB, pA);
-    if (i + 1 >= nseq) return false;
-    tc = seq_tile(i + 1);
-    iteration(SB, B1{}, SB, B0{}, tc * kBN, sA, sB, pA, pB);
+  if (!MASK || nseq > 0) {   // else (a mask left no valid key) o = 0, lse = -inf
+    load_pos(0, std::integral_constant<int, 0>{});
+    load_pos(1, std::integral_constant<int, 1>{});
+    if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    {
+      KFrag kf;
+      read_k(k_of(B0{}), B0{}, kf);
+      sA = qk(kf);
+      read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
+    }
+    int tc = seq_tile(0);
+    // mask words of the tile's second block (mw1) and of the next tile's blocks
+    // (fetched a block ahead: each is a scalar value once it is used)
+    unsigned mw1 = mask_word(tc * kBN + 32);
+    iteration(B0{}, B1{}, B0{}, B0{}, tc * kBN, __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), sA, sB, pA, pB);
     tile_barrier();
-    return true;
-  };
-#if ULYS_ATTN_UNROLL
-  static_assert(kStages == 3, "unrolled ring");
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  for (int i = 0;; i += 3) {
-    if (!step(i, S0{}, S1{}, S2{})) break;
-    if (!step(i + 1, S1{}, S2{}, S0{})) break;
-    if (!step(i + 2, S2{}, S0{}, S1{})) break;
+
+    // Position i (stage SA): its second block, then the first block of
+    // position i+1 (stage SB).  Position i + kStages - 1 is loaded first, into
+    // SP, the stage of position i-1, which every wave has finished with.  The
+    // next tile's key-mask words are fetched a block ahead.  Each step ends
+    // with a barrier.  Returns false after the last position.
+    auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
+      load_pos(i + kStages - 1, SP);
+      const int tn = i + 1 < nseq ? seq_tile(i + 1) : tc;
+      const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
+      iteration(SB, B0{}, SA, B1{}, tc * kBN + 32, __builtin_amdgcn_readfirstlane(mw1), sB, sA, pB, pA);
+      if (i + 1 >= nseq) return false;
+      tc = tn;
+      mw1 = wn1;
+      iteration(SB, B1{}, SB, B0{}, tc * kBN, __builtin_amdgcn_readfirstlane(wn0), sA, sB, pA, pB);
+      tile_barrier();
+      return true;
+    };
+    int sa = 0;
+    for (int i = 0;; ++i) {
+      const int sb = sa == kStages - 1 ? 0 : sa + 1;
+      if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
+      sa = sb;
+    }
+    pv(vf, pA);
   }
-#else
-  int sa = 0;
-  for (int i = 0;; ++i) {
-    const int sb = sa == kStages - 1 ? 0 : sa + 1;
-    if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
-    sa = sb;
-  }
-#endif
-  pv(vf, pA);
 
   // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
   {
     const int row = qrow0 + l32;
     const float l = lane_swap_sum(l_run);
-    const float inv = 1.0f / l;
-    if (row < rows) {
-      uint16_t* op = a.o + ((size_t)b * rows + row) * q_row_stride + (size_t)head * D;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (row < qrows) {
+      uint16_t* op = a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -587,19 +610,18 @@ void attn_fwd_kernel(AttnArgs a) {
           *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
         }
       if (a.lse != nullptr && hh == 0)
-        a.lse[((size_t)b * a.hq + head) * rows + row] = (m_run + __log2f(l)) * kLn2;
+        a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
   }
 }
 
 template <int D, bool FP8>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-#if ULYS_ATTN_XCD
-  dim3 grid(((a.rows + kBM - 1) / kBM) * a.hq * a.batch);
-#else
-  dim3 grid((a.rows + kBM - 1) / kBM, a.hq, a.batch);
-#endif
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8>), grid, dim3(kThreads), 0, s, a);
+  dim3 grid((a.q_rows + kBM - 1) / kBM, a.hq, a.batch);
+  if (a.key_mask != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@ constexpr int kMaxGapBatch = 256;   // batches that may carry a key gap
 constexpr int kMaxPipelineGroups = 64;   // head groups of one ulys_rank_pipeline call
 constexpr int kMaxMergeParts = 16;       // partial results of one ulys_lse_merge call
 constexpr int kAttnRowsPerWorkgroup = 256;   // query rows per attention workgroup (one per CU at a time)
+constexpr int kAttnKeysPerTile = 64;         // keys per attention LDS tile
+constexpr int kMaxMaskTiles = 4096;          // key tiles (262144 keys) an attention call with a key mask may span
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.
@@ -21,7 +23,7 @@ struct RepackGeom {
 };
 
 struct PackArgs {
-  RepackGeom g;
+  RepackGeom g[3];                     // q, k, v (a K/V-only prefix gives q its own geometry)
   const uint16_t* src[3][kMaxDegree];  // q, k, v shards
   void* dst[3];                        // q, k, v slots
   int heads[3];                        // heads of the source tensor (Hq, Hkv, Hkv)
@@ -62,9 +64,11 @@ struct AttnArgs {
   float* lse;
   const float* amax;                   // fp8 q/k: device {amax_q, amax_k}
   float scale;                         // softmax scale (before fp8 descale)
-  int batch, rows, hq, hkv;
+  int batch, q_rows, kv_rows, hq, hkv;
   int has_gap;
   int gap[kMaxGapBatch][2];
+  const uint32_t* key_mask;            // [batch][mask_words] valid-key bits, or null
+  int mask_words;                      // ceil(kv_rows / 32)
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

@@ -10,6 +10,8 @@
 //           t >= R      -> shard (t-R)/S_l, row R + (t-R)%S_l
 //   suffix: t <  P*S_l  -> shard t/S_l, row t%S_l
 //           t >= P*S_l  -> shard r, row S_l + (t - P*S_l)
+// A K/V-only prefix (sglang layer.py _forward_with_replicated_kv_prefix) is
+// the prefix map for k/v and the map without replicated rows for q and o.
 #include "internal.h"
 
 namespace ulys {
@@ -91,8 +93,8 @@ __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
 // + group.  All loads of a thread are issued before its stores.  Chunk indices
 // are 32-bit (the host rejects slots of 2^32 chunks or more).
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
-  const RepackGeom& g = a.g;
-  const int tensor = blockIdx.y / g.ngroups;
+  const int tensor = blockIdx.y / a.g[0].ngroups;
+  const RepackGeom& g = a.g[tensor];
   const int gi = blockIdx.y % g.ngroups;
   const int gh = a.gh[tensor];
   const int D = g.head_dim;
@@ -210,12 +212,12 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   // the largest chunk count over the three tensors sets grid.x
   long most = 0;
   for (int t = 0; t < 3; ++t) {
-    const long cpr = (long)a.gh[t] * a.g.head_dim / (a.fp8[t] ? 16 : 8);
-    const long total = (long)a.g.batch * a.g.rows * cpr;
+    const long cpr = (long)a.gh[t] * a.g[t].head_dim / (a.fp8[t] ? 16 : 8);
+    const long total = (long)a.g[t].batch * a.g[t].rows * cpr;
     if (total > most) most = total;
   }
   const long per_block = (long)kThreads * kPackUnroll;
-  dim3 grid((unsigned)((most + per_block - 1) / per_block), 3 * a.g.ngroups);
+  dim3 grid((unsigned)((most + per_block - 1) / per_block), 3 * a.g[0].ngroups);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -90,3 +90,24 @@ def random_bf16(shape, seed: int, mult: float = 1.0) -> torch.Tensor:
 def bf16_bits(x: torch.Tensor) -> torch.Tensor:
     """Raw 16-bit patterns of a bf16 tensor (for byte-exact comparisons)."""
     return x.contiguous().view(torch.int16)
+
+
+def random_key_mask(batch: int, n_keys: int, seed: int, p_valid: float = 0.5) -> "np.ndarray":
+    """Seeded boolean key mask ``[batch, n_keys]`` (True = valid), each key kept with probability p_valid."""
+    import numpy as np
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return (torch.rand(batch, n_keys, generator=gen) < p_valid).numpy().astype(np.bool_)
+
+
+def key_mask_words(mask) -> torch.Tensor:
+    """Encode a boolean ``[B, N]`` key mask as the library's bit words: int32 ``[B, ceil(N/32)]``,
+    bit ``j % 32`` of word ``j // 32`` set for a valid key ``j`` (an encoding of the input, no arithmetic
+    of the method)."""
+    import numpy as np
+    m = np.asarray(mask, dtype=bool)
+    b, n = m.shape
+    words = (n + 31) // 32
+    padded = np.zeros((b, words * 32), dtype=bool)
+    padded[:, :n] = m
+    w = np.packbits(padded.reshape(b, words, 4, 8), axis=-1, bitorder="little").reshape(b, words, 4)
+    return torch.from_numpy(w.astype(np.uint8).copy()).view(torch.int32).reshape(b, words)

@@ -44,6 +44,9 @@ _lib.ulys_amax_bf16.restype = _i
 _lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
                                    ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
 _lib.ulys_attend_group.restype = _i
+_lib.ulys_attend_group_ex.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
+                                      ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp, _vp]
+_lib.ulys_attend_group_ex.restype = _i
 _lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.POINTER(_vp), _vp]
 _lib.ulys_unpack.restype = _i
 _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -59,18 +62,20 @@ _lib.ulys_strerror.restype = ctypes.c_char_p
 _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge",
-            "ulys_auto_groups", "ulys_strerror", "ulys_last_error")
+EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_unpack",
+            "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror", "ulys_last_error")
+
+ULYS_REP_SUFFIX, ULYS_REP_PREFIX, ULYS_REP_KV_PREFIX = 0, 1, 2
 
 
 @dataclass(frozen=True)
 class Layout:
-    """Python mirror of ``ulys_layout``."""
+    """Python mirror of ``ulys_layout``; ``rep_first`` is a ``ULYS_REP_*`` mode (True/False = prefix/suffix)."""
     batch: int
     degree: int
     s_local: int
     n_rep: int
-    rep_first: bool
+    rep_first: int
     hq: int
     hkv: int
     head_dim: int
@@ -78,11 +83,23 @@ class Layout:
 
     @property
     def rows(self) -> int:
+        """Joint rows of the k/v slots (and of q/o unless the replicated rows are K/V-only)."""
         return self.n_rep + self.degree * self.s_local
 
     @property
     def shard_rows(self) -> int:
+        """Rows of a k/v shard."""
         return self.n_rep + self.s_local
+
+    @property
+    def rows_q(self) -> int:
+        """Joint rows of the q and o slots."""
+        return self.rows - (self.n_rep if int(self.rep_first) == ULYS_REP_KV_PREFIX else 0)
+
+    @property
+    def shard_rows_q(self) -> int:
+        """Rows of a q or o shard."""
+        return self.shard_rows - (self.n_rep if int(self.rep_first) == ULYS_REP_KV_PREFIX else 0)
 
     @property
     def gq(self) -> int:
@@ -145,13 +162,13 @@ def ulys_pack(layout: Layout, rank: int, group: int, q_shards, k_shards, v_shard
     if len(q_shards) != L.degree or len(k_shards) != L.degree or len(v_shards) != L.degree:
         raise ValueError("need one shard per rank for q, k and v")
     ng = L.groups if group < 0 else 1
-    nq = L.batch * L.shard_rows * L.hq * L.head_dim
+    nq = L.batch * L.shard_rows_q * L.hq * L.head_dim
     nkv = L.batch * L.shard_rows * L.hkv * L.head_dim
     qa = _ptrs(q_shards, "q_shards", _BF16, nq)
     ka = _ptrs(k_shards, "k_shards", _BF16, nkv)
     va = _ptrs(v_shards, "v_shards", _BF16, nkv)
     qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
-    qs = _dev(q_slot, "q_slot", qk_t, ng * L.batch * L.rows * L.gq * L.head_dim)
+    qs = _dev(q_slot, "q_slot", qk_t, ng * L.batch * L.rows_q * L.gq * L.head_dim)
     ks = _dev(k_slot, "k_slot", qk_t, ng * L.batch * L.rows * L.gkv * L.head_dim)
     vs = _dev(v_slot, "v_slot", _BF16, ng * L.batch * L.rows * L.gkv * L.head_dim)
     am = None
@@ -199,14 +216,49 @@ def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
                                   _stream(stream)))
 
 
+def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                         lse: torch.Tensor | None = None, softmax_scale: float = 0.0, key_gaps=None,
+                         key_mask: torch.Tensor | None = None, qk_dtype: int = ULYS_BF16,
+                         qk_amax: torch.Tensor | None = None, stream=None) -> None:
+    """Attention with q ``[B, Nq, hq, D]`` and k/v ``[B, Nk, hkv, D]`` (Nq may differ from Nk) -> o ``[B, Nq, hq, D]``
+    (and lse ``[B, hq, Nq]``).
+
+    ``key_mask``: device int32/uint32 words ``[B, ceil(Nk/32)]``, bit ``j % 32`` of word ``j // 32`` set for a
+    valid key ``j``, or None (all keys valid).  ``key_gaps`` as for :func:`ulys_attend_group`.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
+    b, nq, hq, d = q.shape
+    nk, hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (b, nk, hkv, d) or tuple(v.shape) != (b, nk, hkv, d) or tuple(o.shape) != (b, nq, hq, d):
+        raise ValueError("shape mismatch between q, k, v and o")
+    qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
+    qp = _dev(q, "q", qk_t)
+    kp = _dev(k, "k", qk_t)
+    vp = _dev(v, "v", _BF16)
+    op = _dev(o, "o", _BF16)
+    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), b * hq * nq)
+    am = None if qk_amax is None else _dev(qk_amax, "qk_amax", (torch.float32,), 2)
+    mp = None
+    if key_mask is not None:
+        mp = _dev(key_mask, "key_mask", (torch.int32, torch.uint32), b * ((nk + 31) // 32))
+    gaps = None
+    if key_gaps is not None:
+        if len(key_gaps) != b:
+            raise ValueError("key_gaps needs one (start, end) per batch")
+        gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
+    _check(_lib.ulys_attend_group_ex(b, nq, nk, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, mp,
+                                     op, lp, _stream(stream)))
+
+
 def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_shards, stream=None) -> None:
     """Scatter the output slot(s) of (rank, group) into the P output shards."""
     L = layout
     if len(o_shards) != L.degree:
         raise ValueError("need one output shard per rank")
     ng = L.groups if group < 0 else 1
-    sp = _dev(o_slot, "o_slot", _BF16, ng * L.batch * L.rows * L.gq * L.head_dim)
-    oa = _ptrs(o_shards, "o_shards", _BF16, L.batch * L.shard_rows * L.hq * L.head_dim)
+    sp = _dev(o_slot, "o_slot", _BF16, ng * L.batch * L.rows_q * L.gq * L.head_dim)
+    oa = _ptrs(o_shards, "o_shards", _BF16, L.batch * L.shard_rows_q * L.hq * L.head_dim)
     c = L.c_struct()
     _check(_lib.ulys_unpack(ctypes.byref(c), rank, group, sp, oa, _stream(stream)))
 
@@ -217,7 +269,7 @@ def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, 
                        stream=None, copy_stream=None) -> None:
     """Pack, attend and unpack every head group of ``rank``; repack on ``copy_stream`` overlaps attention.
 
-    Slots hold all G groups (``[G, B, rows, Gh, D]``), lse ``[G, B, Gq, rows]`` or None.
+    Slots hold all G groups (``[G, B, rows, Gh, D]``; q/o with ``rows_q`` rows), lse ``[G, B, Gq, rows_q]`` or None.
     ``copy_stream`` None means the same stream as ``stream`` (sequential).
     """
     L = layout
@@ -226,18 +278,18 @@ def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, 
     if len(o_shards) != L.degree:
         raise ValueError("need one output shard per rank")
     G = L.groups
-    nq = L.batch * L.shard_rows * L.hq * L.head_dim
+    nq = L.batch * L.shard_rows_q * L.hq * L.head_dim
     nkv = L.batch * L.shard_rows * L.hkv * L.head_dim
     qa = _ptrs(q_shards, "q_shards", _BF16, nq)
     ka = _ptrs(k_shards, "k_shards", _BF16, nkv)
     va = _ptrs(v_shards, "v_shards", _BF16, nkv)
     qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
-    qs = _dev(q_slots, "q_slots", qk_t, G * L.batch * L.rows * L.gq * L.head_dim)
+    qs = _dev(q_slots, "q_slots", qk_t, G * L.batch * L.rows_q * L.gq * L.head_dim)
     ks = _dev(k_slots, "k_slots", qk_t, G * L.batch * L.rows * L.gkv * L.head_dim)
     vs = _dev(v_slots, "v_slots", _BF16, G * L.batch * L.rows * L.gkv * L.head_dim)
-    os_ = _dev(o_slots, "o_slots", _BF16, G * L.batch * L.rows * L.gq * L.head_dim)
+    os_ = _dev(o_slots, "o_slots", _BF16, G * L.batch * L.rows_q * L.gq * L.head_dim)
     oa = _ptrs(o_shards, "o_shards", _BF16, nq)
-    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), G * L.batch * L.gq * L.rows)
+    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), G * L.batch * L.gq * L.rows_q)
     am = None if qk_amax is None else _dev(qk_amax, "qk_amax", (torch.float32,), 2)
     gaps = None
     if key_gaps is not None:
