@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+ATTN_KERNEL = "attn_fwd_kernel<128, false, false>"   # D = 128, bf16 q/k, no key mask
 
 
 def parse():
@@ -40,12 +41,15 @@ def parse():
                     help="time ulys_rank_pipeline (per-group repack on a second stream overlapping attention) "
                          "instead of the one-stream step (pack all groups, attend each, unpack all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows the oracle computes for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=12288, help="query rows the oracle computes for cpu_baseline")
     ap.add_argument("--group-sweep", action="store_true",
                     help="time a rank's 10 heads (D=128) as G = 1, 2, 5, 10 attention calls for several sequence "
                          "lengths and print the automatic group count beside (calibrates ulys_auto_groups)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (HBM byte-counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="read the rocprofv3 runs under DIR (stats_g{1,5}, fetch_/write_ g1, g5 and copy), "
+                         "write profiles/attn_fwd_traffic.json and print the summary tables (no GPU needed)")
     return ap.parse_args()
 
 
@@ -171,6 +175,85 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
+def summarize_profiles(d: str):
+    """rocprofv3 runs -> profiles/attn_fwd_traffic.json + markdown tables on stdout.
+
+    Expects under ``d``: stats_g1, stats_g5 (``--kernel-trace --stats``), fetch_g1, write_g1,
+    fetch_g5, write_g5 (``--pmc FETCH_SIZE`` / ``WRITE_SIZE`` of the bench at G = 1, 5) and
+    fetch_copy, write_copy (the same counters on ``--copy-calibration``), each with
+    ``-o run --output-format csv``."""
+    import csv
+    import statistics
+
+    def rows_of(sub, fname):
+        path = os.path.join(d, sub, fname)
+        with open(path) as fh:
+            return list(csv.DictReader(fh))
+
+    def counter(sub, name, kernel_substr):
+        vals = {}
+        for r in rows_of(sub, "run_counter_collection.csv"):
+            if r["Counter_Name"] == name and kernel_substr in r["Kernel_Name"]:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {name} rows for {kernel_substr} in {sub}")
+        return statistics.mean(vals.values()), len(vals)
+
+    attn = "attn_fwd_kernel<128, false, false>"
+    print("## Kernel statistics (rocprofv3 --kernel-trace --stats)\n")
+    for G in (1, 5):
+        print(f"### G = {G}\n\n| kernel | calls | total ms | avg us | min us | max us | % |\n|---|---|---|---|---|---|---|")
+        for r in rows_of(f"stats_g{G}", "run_kernel_stats.csv"):
+            name = r["Name"].replace("ulys::(anonymous namespace)::", "").replace("(ulys::AttnArgs)", "")
+            print(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                  f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        print()
+    fcopy, ncopy = counter("fetch_copy", "FETCH_SIZE", "copyBuffer")
+    wcopy, _ = counter("write_copy", "WRITE_SIZE", "copyBuffer")
+    n = 1 << 30
+    fscale, wscale = n / (fcopy * 1024), n / (wcopy * 1024)
+    out = {"kernel": attn,
+           "workload": "Wan2.1 Ulysses-4 share: q/k/v slots [1,27280,10/G,128] bf16, non-causal, LSE",
+           "source_sha256": kernel_source_hash(),
+           "calibration": {"copy": f"__amd_rocclr_copyBuffer of 1 GiB (torch copy_), {ncopy} dispatches",
+                           "fetch_kib_per_dispatch": round(fcopy, 3), "write_kib_per_dispatch": round(wcopy, 3),
+                           "fetch_bytes_per_counted_byte": round(fscale, 5),
+                           "write_bytes_per_counted_byte": round(wscale, 5)},
+           "per_groups": {}}
+    print("## HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE; scaled by the 1 GiB copy)\n")
+    print(f"Calibration: FETCH_SIZE {fcopy:.1f} KiB and WRITE_SIZE {wcopy:.1f} KiB per 1 GiB copy "
+          f"-> {fscale:.5f} and {wscale:.5f} bytes per counted byte.\n")
+    print("| kernel | G | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | write bytes | algorithmic read / write | read / algorithmic |")
+    print("|---|---|---|---|---|---|---|---|")
+    rows = 27280
+    for G in (1, 5):
+        heads = 10 // G
+        f, _ = counter(f"fetch_g{G}", "FETCH_SIZE", attn)
+        w_, _ = counter(f"write_g{G}", "WRITE_SIZE", attn)
+        rd, wr = f * 1024 * fscale, w_ * 1024 * wscale
+        alg_r = 3 * rows * heads * 128 * 2
+        alg_w = rows * heads * 128 * 2 + rows * heads * 4
+        out["per_groups"][str(G)] = {"heads_per_launch": heads, "fetch_kib_per_dispatch": round(f, 2),
+                                     "write_kib_per_dispatch": round(w_, 2), "hbm_read_bytes": int(rd),
+                                     "hbm_write_bytes": int(wr), "hbm_bytes_per_launch": int(rd + wr),
+                                     "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+                                     "read_over_algorithmic": round(rd / alg_r, 2)}
+        print(f"| `{attn}` | {G} | {f:.1f} | {w_:.1f} | {rd:.4g} | {wr:.4g} | {alg_r:.4g} / {alg_w:.4g} | "
+              f"{rd / alg_r:.2f} |")
+        for kname, alg in (("pack_kernel", None), ("unpack_kernel", None)):
+            try:
+                fk, nk = counter(f"fetch_g{G}", "FETCH_SIZE", kname)
+                wk, _ = counter(f"write_g{G}", "WRITE_SIZE", kname)
+            except SystemExit:
+                continue
+            print(f"| `{kname}` | {G} | {fk:.1f} | {wk:.1f} | {fk * 1024 * fscale:.4g} | {wk * 1024 * wscale:.4g} | | |")
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(f"\nwrote {TRAFFIC_FILE}")
+
+
 def cpu_baseline(q, k, v, rows_sample: int):
     """The oracle as it stands (fp64 NumPy), on a bounded sample of the same workload:
     attention for `rows_sample` query rows of all 10 heads of rank 0 over all 27280 keys."""
@@ -200,6 +283,9 @@ def cpu_baseline(q, k, v, rows_sample: int):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -320,7 +406,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(G), "kernel": "attn_fwd_kernel<128,false>",
+                     "traffic": measured_traffic(G), "kernel": ATTN_KERNEL,
                      "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
     }
     res["lse_merge_gbs"] = round(merge_gbs(torch, ulys, os_, lse, args.steps), 1)
