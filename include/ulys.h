@@ -227,6 +227,17 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * Rules: rows >= 1, hq % hkv == 0, head_dim in {64, 128}.  Each head's
  * result depends only on that head's data: calling on a head subset gives
  * the same bytes for those heads as the full call.
+ *
+ * Key-range split (automatic, see ulys_attend_splits): when the query tiles
+ * of a call are too few to keep every compute unit busy, each (b, head,
+ * 256-row query tile) is computed as C workgroups over C contiguous runs of
+ * its 64-key tiles, each writing an fp32 partial (o, lse); a second kernel
+ * combines them in run order with the log-sum-exp weights.  C depends on
+ * (batch, rows, the device's compute units) only, so the head-subset rule
+ * above still holds.  The partials live in a device workspace that the
+ * library allocates per (device, stream) on first use and keeps (at most
+ * 2 GiB; a call needing more runs its heads in several launches); calls on
+ * one stream share it in stream order.
  */
 int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       const void* q, const void* k, const void* v, int qk_dtype,
@@ -255,15 +266,41 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  * so this cannot be rejected up front).  Query rows are never masked.
  * Rules: as ulys_attend_group with q_rows, kv_rows >= 1; key_mask 4-byte
  * aligned; with a key mask kv_rows <= 262144 (ULYS_EUNSUPPORTED otherwise).
+ * key_splits: 0 = automatic (ulys_attend_splits of the device), 1 = no
+ * split, 2..16 = that many key-range runs (outside [0, 16]: ULYS_EINVAL);
+ * runs are near-equal shares of the processed key tiles, and a run without
+ * tiles contributes nothing.
  * ulys_attend_group(B, rows, ...) equals ulys_attend_group_ex(B, rows, rows,
- * ..., key_mask = NULL, ...), and a mask that marks exactly the keys outside
- * the gaps gives the same bytes as the gaps.
+ * ..., key_mask = NULL, key_splits = 0, ...), and a mask that marks exactly
+ * the keys outside the gaps gives the same bytes as the gaps (at equal
+ * key_splits).
  */
 int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim,
                          const void* q, const void* k, const void* v, int qk_dtype,
                          float softmax_scale, const float* qk_amax,
-                         const int32_t* key_gaps, const uint32_t* key_mask,
+                         const int32_t* key_gaps, const uint32_t* key_mask, int key_splits,
                          void* o, float* lse, void* stream);
+
+/*
+ * ulys_attend_splits -- the automatic key-range split of an attention call.
+ *
+ * Source: the per-rank attention over the full gathered sequence (sglang
+ * PR #43521, "Receive slots"; flashdreams cp.py torch_sdpa_*) is one launch
+ * whose workgroup count is fixed by the shape; the split and its merge are
+ * the log-sum-exp combination of partial attentions over disjoint key sets
+ * (flashdreams cp.py, ContextParallelAttention._impl_ring).
+ *
+ * Returns the run count C >= 1 that ulys_attend_group uses for
+ * (batch, q_rows, kv_rows) on a device with compute_units CUs: the C in
+ * [1, 16] (each run >= 16 key tiles) minimising a model of the launch time
+ * averaged over calls of 2, 4, 8 and 16 heads, if it beats C = 1 by 3%.
+ * The model: workgroups run in rounds of one per CU, with the device's
+ * throughput saturating at 84% of its CUs busy; a run costs 1/C of the keys
+ * plus about six key tiles of start-up; the merge moves 4C + 2 bytes per
+ * output element.  Host-only: enqueues nothing.  A negative status
+ * (ULYS_EINVAL) if an argument is < 1.
+ */
+int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units);
 
 /*
  * ulys_unpack -- inverse of ulys_pack for the output of (rank, group).
@@ -296,7 +333,7 @@ int ulys_unpack(const ulys_layout* layout, int rank, int group,
  *
  * Equivalent to, for g = 0 .. G-1 in order:
  *   ulys_pack(layout, rank, g, ...) into slot g,
- *   ulys_attend_group_ex(B, rows_q, rows_kv, Gq, Gkv, D, slot g ..., o slot g, lse g),
+ *   ulys_attend_group_ex(B, rows_q, rows_kv, Gq, Gkv, D, slot g ..., key_splits 0, o slot g, lse g),
  *   ulys_unpack(layout, rank, g, o slot g, o_shards)
  * and byte-identical to it.  q/k/v/o_slots hold G consecutive slots
  * ([G][B, rows, Gh, D], the group = -1 layout of ulys_pack); lse is

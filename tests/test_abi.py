@@ -28,7 +28,8 @@ def _declared():
 
 def test_header_declares_the_path():
     names = _declared()
-    for n in ("ulys_pack", "ulys_attend_group", "ulys_attend_group_ex", "ulys_unpack", "ulys_rank_pipeline",
+    for n in ("ulys_pack", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits", "ulys_unpack",
+              "ulys_rank_pipeline",
               "ulys_lse_merge", "ulys_auto_groups", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
         assert n in names
 
@@ -122,12 +123,12 @@ def test_attend_rules(U):
     assert _attend(U, batch=300, gaps=[0, 1] * 300) == -1             # too many gap batches
 
 
-def _attend_ex(U, batch=1, nq=100, nk=140, hq=2, hkv=2, d=128, dtype=0, gaps=None, mask=None):
+def _attend_ex(U, batch=1, nq=100, nk=140, hq=2, hkv=2, d=128, dtype=0, gaps=None, mask=None, splits=0):
     g = None
     if gaps is not None:
         g = (ctypes.c_int32 * len(gaps))(*gaps)
     return U.call_raw("ulys_attend_group_ex", batch, nq, nk, hq, hkv, d, FAKE, FAKE, FAKE, dtype, ctypes.c_float(0.0),
-                      None, g, mask, FAKE, None, None)
+                      None, g, mask, splits, FAKE, None, None)
 
 
 def test_attend_ex_rules(U):
@@ -140,6 +141,29 @@ def test_attend_ex_rules(U):
     assert _attend_ex(U, mask=FAKE + 2) == -1                          # mask words 4-byte aligned
     assert _attend_ex(U, nk=262144 + 64, mask=FAKE) == -2              # key-mask tile list limit
     assert "key mask" in U.last_error()
+    assert _attend_ex(U, splits=-1) == -1                              # key_splits in [0, 16]
+    assert _attend_ex(U, splits=17) == -1
+    assert "key_splits" in U.last_error()
+
+
+def test_attend_splits_rule(U):
+    """The automatic key-range split: host arithmetic only."""
+    # the Wan share, 107 query tiles per head on 256 CUs: no split (measured: 2 or 7 runs are 4% slower for a
+    # 2-head call, whose 214 workgroups already reach the device's saturated throughput)
+    assert U.ulys_attend_splits(1, 27280, 27280, 256) == 1
+    # a short sequence, 6 query tiles per head: 5 runs of 19 key tiles
+    assert U.ulys_attend_splits(1, 1500, 6000, 256) == 5
+    # few keys: no run would reach 16 tiles of 64 keys
+    assert U.ulys_attend_splits(1, 256, 1000, 256) == 1
+    assert U.ulys_attend_splits(1, 1000, 2047, 256) == 2                 # 32 tiles: two runs of 16
+    # many query tiles already fill the CUs (4096 tiles)
+    assert U.ulys_attend_splits(16, 65536, 65536, 256) == 1
+    for args in [(1, 27280, 27280, 256), (2, 5000, 90000, 256), (1, 300, 300000, 80), (4, 8192, 8192, 304)]:
+        c = U.ulys_attend_splits(*args)
+        assert 1 <= c <= 16
+        assert c == 1 or (args[2] + 63) // 64 >= 16 * c
+    assert U.call_raw("ulys_attend_splits", 0, 1, 1, 1) == -1
+    assert U.call_raw("ulys_attend_splits", 1, 1, 1, 0) == -1
 
 
 def test_unpack_and_amax_rules(U):

@@ -97,6 +97,69 @@ int hip_status(hipError_t e) {
   return fail(ULYS_EHIP, "HIP: %s", hipGetErrorString(e));
 }
 
+// Automatic key-range split of an attention call: the run count C that
+// minimises a model of the launch time, averaged over calls of 2, 4, 8 and 16
+// heads (the head counts of pipeline groups; the choice must not depend on the
+// head count, so that a call over a subset of the heads reproduces the full
+// call's bytes), kept only if it beats no split by 3%.  Model, in units of one
+// workgroup's time over all keys (measured on MI355X: a 2-head call at the
+// 27280-row shape runs 4% slower with 2 or 7 runs, a 10-head call 7% faster
+// with 2 or 4 runs):
+//  * workgroups run in rounds of one per CU, but the device's throughput
+//    saturates at about 84% of its CUs busy (the clock drops as more CUs
+//    work), so a full round takes 1/0.84 of a partly filled one;
+//  * a run costs 1/C of the keys plus about six key tiles of start-up
+//    (Q load, pipeline fill, partial write);
+//  * the merge moves 4C + 2 bytes per output element at an HBM rate of 1.25
+//    times the per-CU attention rate in bytes per flop.
+int auto_splits(long long batch, long long q_rows, long long kv_rows, int cus) {
+  const double units = (double)batch * ((q_rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup);
+  const double nt = (double)((kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile);
+  const double kSaturation = 0.84, kStartTiles = 6.0, kMinTilesPerChunk = 16.0, kGain = 0.97;
+  const double n_sat = kSaturation * cus;
+  auto cost = [&](int c, int hq) {
+    const double wgs = units * c * hq;
+    const double full = floor(wgs / cus), rest = wgs - full * cus;
+    const double per = 1.0 / c + kStartTiles / nt;
+    double t = full * (cus / n_sat) * per;
+    if (rest > 0) t += per * fmax(1.0, rest / n_sat);
+    if (c > 1) t += hq * units * (4.0 * c + 2.0) / (320.0 * nt);
+    return t;
+  };
+  static const int kHeads[] = {2, 4, 8, 16};
+  int best = 1;
+  double best_cost = 1.0;
+  for (int c = 2; c <= ulys::kMaxKeySplits && nt >= c * kMinTilesPerChunk; ++c) {
+    double rel = 0.0;
+    for (int hq : kHeads) rel += cost(c, hq) / cost(1, hq);
+    rel /= (double)(sizeof kHeads / sizeof kHeads[0]);
+    if (rel < kGain * best_cost) {
+      best = c;
+      best_cost = rel;
+    }
+  }
+  return best;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus(int* cus) {
+  static int cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *cus = cache[dev];
+    return ULYS_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (n < 1) return fail(ULYS_EHIP, "device reports %d compute units", n);
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *cus = n;
+  return ULYS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,7 +206,8 @@ int prepare_pack(const ulys_layout* L, int rank, int group, const void* const* q
 // Validated launch arguments of an attention call; nothing is enqueued.
 int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim, const void* q, const void* k,
                    const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
-                   const int32_t* key_gaps, const uint32_t* key_mask, void* o, float* lse, ulys::AttnArgs& a) {
+                   const int32_t* key_gaps, const uint32_t* key_mask, int key_splits, void* o, float* lse,
+                   ulys::AttnArgs& a) {
   if (batch < 1 || q_rows < 1 || kv_rows < 1 || hq < 1 || hkv < 1)
     return fail(ULYS_EINVAL, "batch, q_rows, kv_rows, hq and hkv must be >= 1");
   if (hq % hkv) return fail(ULYS_EINVAL, "hq %d must be a multiple of hkv %d", hq, hkv);
@@ -163,6 +227,8 @@ int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head
   if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(ULYS_EINVAL, "softmax_scale must be finite");
+  if (key_splits < 0 || key_splits > ulys::kMaxKeySplits)
+    return fail(ULYS_EINVAL, "key_splits %d outside [0, %d]", key_splits, ulys::kMaxKeySplits);
   if (key_mask != nullptr) {
     if ((uintptr_t)key_mask & 3u) return fail(ULYS_EINVAL, "key_mask is not 4-byte aligned");
     const long long tiles = ((long long)kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile;
@@ -198,6 +264,18 @@ int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head
   a.hkv = hkv;
   a.key_mask = key_mask;
   a.mask_words = (kv_rows + 31) / 32;
+  a.splits = key_splits;   // 0: resolved by resolve_splits once every rule has been checked
+  return ULYS_OK;
+}
+
+// The automatic key-range split (from the device's compute units and the
+// shape) of validated arguments; the first HIP call of an attention call.
+int resolve_splits(ulys::AttnArgs& a) {
+  if (a.splits != 0) return ULYS_OK;
+  int cus = 0;
+  const int st = device_cus(&cus);
+  if (st) return st;
+  a.splits = auto_splits(a.batch, a.q_rows, a.kv_rows, cus);
   return ULYS_OK;
 }
 
@@ -253,19 +331,20 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const 
                       const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
                       const int32_t* key_gaps, void* o, float* lse, void* stream) {
   ulys::AttnArgs a;
-  const int st = prepare_attend(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax,
-                                key_gaps, nullptr, o, lse, a);
-  if (st) return st;
+  int st = prepare_attend(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax,
+                          key_gaps, nullptr, 0, o, lse, a);
+  if (st || (st = resolve_splits(a))) return st;
   return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
 }
 
 int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim, const void* q,
                          const void* k, const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
-                         const int32_t* key_gaps, const uint32_t* key_mask, void* o, float* lse, void* stream) {
+                         const int32_t* key_gaps, const uint32_t* key_mask, int key_splits, void* o, float* lse,
+                         void* stream) {
   ulys::AttnArgs a;
-  const int st = prepare_attend(batch, q_rows, kv_rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale,
-                                qk_amax, key_gaps, key_mask, o, lse, a);
-  if (st) return st;
+  int st = prepare_attend(batch, q_rows, kv_rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale,
+                          qk_amax, key_gaps, key_mask, key_splits, o, lse, a);
+  if (st || (st = resolve_splits(a))) return st;
   return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
 }
 
@@ -291,10 +370,11 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
   const int gq = L->hq / L->degree / G, gkv = L->hkv / L->degree / G;
   ulys::AttnArgs at;
   if ((st = prepare_attend(L->batch, q_rows, kv_rows, gq, gkv, L->head_dim, q_slots, k_slots, v_slots, qk_dtype,
-                           softmax_scale, qk_amax, key_gaps, nullptr, o_slots, lse, at)))
+                           softmax_scale, qk_amax, key_gaps, nullptr, 0, o_slots, lse, at)))
     return st;
   if (G > ulys::kMaxPipelineGroups)
     return fail(ULYS_EUNSUPPORTED, "pipeline of %d groups exceeds %d", G, ulys::kMaxPipelineGroups);
+  if ((st = resolve_splits(at))) return st;
   const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
   const size_t qk_elem = fp8 ? 1 : 2;
   const size_t elems_q = (size_t)L->batch * q_rows * gq * L->head_dim;
@@ -404,6 +484,13 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
   a.heads = heads;
   a.head_dim = head_dim;
   return hip_status(ulys::launch_lse_merge(a, (hipStream_t)stream));
+}
+
+int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units) {
+  if (batch < 1 || q_rows < 1 || kv_rows < 1 || compute_units < 1)
+    return fail(ULYS_EINVAL, "batch, q_rows, kv_rows and compute_units must be >= 1");
+  ok();
+  return auto_splits(batch, q_rows, kv_rows, compute_units);
 }
 
 int ulys_auto_groups(const ulys_layout* L, int compute_units) {

@@ -41,7 +41,11 @@
 //    that straddle the gap are masked per element.
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -53,6 +57,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -146,8 +151,10 @@ void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int qtile = blockIdx.x;
-  const int head = blockIdx.y;
+  const int split = blockIdx.x / a.qtiles;   // key-range chunk of this workgroup
+  const int qtile = blockIdx.x - split * a.qtiles;
+  const int hl = blockIdx.y;                  // head within this launch
+  const int head = a.head0 + hl;
   const int b = blockIdx.z;
   const int qrows = a.q_rows;
   const int rows = a.kv_rows;   // keys
@@ -533,16 +540,22 @@ void attn_fwd_kernel(AttnArgs a) {
         tile_list[pos++] = (unsigned short)t;
     __syncthreads();
   }
+  // This workgroup's chunk of the sequence: positions [p0, p0 + n), the
+  // split-th of `splits` near-equal runs (a function of the tile sequence
+  // alone, the same for every head).
+  const int p0 = (int)(((long long)split * nseq) / a.splits);
+  const int n = (int)(((long long)(split + 1) * nseq) / a.splits) - p0;
   // (uniform across the workgroup: kept in scalar registers)
   auto seq_tile = [&](int pos) {
+    pos += p0;
     if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
     else return pos < skip_first ? pos : pos + nskip;
   };
   // Position pos goes to stage pos % kStages; past the end the last tile is
   // loaded again, which keeps every wave's load count per tile uniform.
-  auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, nseq - 1)), st); };
+  auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, n - 1)), st); };
 
-  if (!MASK || nseq > 0) {   // else (a mask left no valid key) o = 0, lse = -inf
+  if (n > 0) {   // else (an empty chunk, or a mask that left no valid key) o = 0, lse = -inf
     load_pos(0, std::integral_constant<int, 0>{});
     load_pos(1, std::integral_constant<int, 1>{});
     if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
@@ -570,10 +583,10 @@ void attn_fwd_kernel(AttnArgs a) {
     // with a barrier.  Returns false after the last position.
     auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
       load_pos(i + kStages - 1, SP);
-      const int tn = i + 1 < nseq ? seq_tile(i + 1) : tc;
+      const int tn = i + 1 < n ? seq_tile(i + 1) : tc;
       const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
       iteration(SB, B0{}, SA, B1{}, tc * kBN + 32, __builtin_amdgcn_readfirstlane(mw1), sB, sA, pB, pA);
-      if (i + 1 >= nseq) return false;
+      if (i + 1 >= n) return false;
       tc = tn;
       mw1 = wn1;
       iteration(SB, B1{}, SB, B0{}, tc * kBN, __builtin_amdgcn_readfirstlane(wn0), sA, sB, pA, pB);
@@ -590,11 +603,26 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
+  // (with a key-range split: o in fp32 and lse in the log2 domain, per split)
   {
     const int row = qrow0 + l32;
     const float l = lane_swap_sum(l_run);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (row < qrows) {
+    if (row < qrows && a.splits > 1) {
+      const size_t prow = ((size_t)split * a.batch + b) * qrows + row;
+      float* pp = a.part_o + (prow * a.hsub + hl) * D;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                            o[db][4 * r4 + 3] * inv};
+          *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
+        }
+      if (hh == 0)
+        a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] =
+            l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+    } else if (row < qrows) {
       uint16_t* op = a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
@@ -615,14 +643,148 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Merge of the key-range splits of one launch, in split order (fixed, so the
+// result does not depend on which workgroup finished first):
+//   M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
+//   lse = (M + log2 sum_s w_s) ln 2,
+// the exact combination of softmaxes over disjoint key sets (lse_s in the log2
+// domain; a split with no key has lse_s = -inf and weight 0; if every split is
+// empty, o = 0 and lse = -inf).  One thread per 8 head-dim elements of a
+// (b, row, head): 2 x 16-byte fp32 reads per split, one 16-byte bf16 write.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(AttnArgs a) {
+  constexpr int kCpr = D / 8;   // threads per (b, row, head)
+  const size_t total = (size_t)a.batch * a.q_rows * a.hsub * kCpr;
+  const size_t idx = (size_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % kCpr);
+  const size_t rh = idx / kCpr;               // (b * q_rows + row) * hsub + hl
+  const int hl = (int)(rh % a.hsub);
+  const size_t br = rh / a.hsub;              // b * q_rows + row
+  const int row = (int)(br % a.q_rows);
+  const int b = (int)(br / a.q_rows);
+  const size_t split_o = (size_t)a.batch * a.q_rows * a.hsub * D;       // floats per split
+  const size_t split_l = (size_t)a.batch * a.hsub * a.q_rows;
+  const size_t li = ((size_t)b * a.hsub + hl) * a.q_rows + row;
+
+  float lv[kMaxKeySplits];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplits; ++s)
+    if (s < a.splits) {
+      lv[s] = a.part_lse[s * split_l + li];
+      mx = fmaxf(mx, lv[s]);
+    }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.0f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kMaxKeySplits; ++s)
+      if (s < a.splits) {
+        const float w = __builtin_amdgcn_exp2f(lv[s] - mx);   // 0 for an empty split
+        const f32x4* src = (const f32x4*)(a.part_o + s * split_o + rh * D + 8 * c);
+        const f32x4 x0 = __builtin_nontemporal_load(src), x1 = __builtin_nontemporal_load(src + 1);
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += w * x0[i];
+          acc[4 + i] += w * x1[i];
+        }
+        wsum += w;
+      }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 v = {acc[2 * i] * inv, acc[2 * i + 1] * inv};
+    out[i] = __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
+  }
+  const int head = a.head0 + hl;
+  *(u32x4*)(a.o + (br * a.hq + head) * D + 8 * c) = out;
+  if (a.lse != nullptr && c == 0)
+    a.lse[((size_t)b * a.hq + head) * a.q_rows + row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 template <int D, bool FP8>
-hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.q_rows + kBM - 1) / kBM, a.hq, a.batch);
+hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.qtiles * a.splits, a.hsub, a.batch);
   if (a.key_mask != nullptr)
     hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, true>), grid, dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, false>), grid, dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const size_t threads = (size_t)a.batch * a.q_rows * a.hsub * (D / 8);
+  hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)((threads + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// Split workspace of one (device, stream): calls on one stream run in order,
+// so they may share it; calls on different streams get their own.  Grown on
+// demand, kept until the process ends.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+hipError_t split_workspace(hipStream_t s, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, (uintptr_t)s}];
+  if (w.bytes < bytes) {
+    if (w.ptr != nullptr) {
+      // earlier calls on this stream may still read the old buffer
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+      if ((e = hipFree(w.ptr)) != hipSuccess) return e;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if ((e = hipMalloc(&w.ptr, bytes)) != hipSuccess) {
+      w.ptr = nullptr;
+      return e;
+    }
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return hipSuccess;
+}
+
+// Largest split workspace one call uses; a call whose heads need more runs
+// as several launches over head ranges (each head's bytes are unchanged).
+constexpr size_t kSplitWorkspaceCap = size_t(2) << 30;
+
+template <int D, bool FP8>
+hipError_t launch(const AttnArgs& in, hipStream_t s) {
+  AttnArgs a = in;
+  a.qtiles = (a.q_rows + kBM - 1) / kBM;
+  a.head0 = 0;
+  a.hsub = a.hq;
+  if (a.splits <= 1) {
+    a.splits = 1;
+    return launch_one<D, FP8>(a, s);
+  }
+  const size_t o_per_head = (size_t)a.splits * a.batch * a.q_rows * D * sizeof(float);
+  const size_t l_per_head = (size_t)a.splits * a.batch * a.q_rows * sizeof(float);
+  const size_t per_head = o_per_head + l_per_head;
+  const int hsub = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.hq, kSplitWorkspaceCap / per_head));
+  void* ws = nullptr;
+  hipError_t e = split_workspace(s, per_head * hsub, &ws);
+  if (e != hipSuccess) return e;
+  a.part_o = (float*)ws;
+  a.part_lse = (float*)((char*)ws + o_per_head * hsub);
+  for (int h0 = 0; h0 < a.hq; h0 += hsub) {
+    a.head0 = h0;
+    a.hsub = std::min(hsub, a.hq - h0);
+    if ((e = launch_one<D, FP8>(a, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

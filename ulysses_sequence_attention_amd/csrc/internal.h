@@ -14,6 +14,7 @@ constexpr int kMaxMergeParts = 16;       // partial results of one ulys_lse_merg
 constexpr int kAttnRowsPerWorkgroup = 256;   // query rows per attention workgroup (one per CU at a time)
 constexpr int kAttnKeysPerTile = 64;         // keys per attention LDS tile
 constexpr int kMaxMaskTiles = 4096;          // key tiles (262144 keys) an attention call with a key mask may span
+constexpr int kMaxKeySplits = 16;            // key-range chunks per query tile
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.
@@ -69,6 +70,15 @@ struct AttnArgs {
   int gap[kMaxGapBatch][2];
   const uint32_t* key_mask;            // [batch][mask_words] valid-key bits, or null
   int mask_words;                      // ceil(kv_rows / 32)
+  // Key-range split: `splits` workgroups share a (b, head, query tile), each
+  // taking a contiguous run of its key tiles; with splits > 1 each writes its
+  // fp32 result (o normalised, lse in the log2 domain) to part_o
+  // [splits][batch][q_rows][hsub][D] / part_lse [splits][batch][hsub][q_rows]
+  // and a merge kernel combines them in split order.  One launch covers heads
+  // [head0, head0 + hsub).
+  int splits, qtiles, head0, hsub;
+  float* part_o;
+  float* part_lse;
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

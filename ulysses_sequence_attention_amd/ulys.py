@@ -45,8 +45,10 @@ _lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes
                                    ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
 _lib.ulys_attend_group.restype = _i
 _lib.ulys_attend_group_ex.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
-                                      ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp, _vp]
+                                      ctypes.POINTER(ctypes.c_int32), _vp, _i, _vp, _vp, _vp]
 _lib.ulys_attend_group_ex.restype = _i
+_lib.ulys_attend_splits.argtypes = [_i, _i, _i, _i]
+_lib.ulys_attend_splits.restype = _i
 _lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.POINTER(_vp), _vp]
 _lib.ulys_unpack.restype = _i
 _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -62,8 +64,9 @@ _lib.ulys_strerror.restype = ctypes.c_char_p
 _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
-EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_unpack",
-            "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror", "ulys_last_error")
+EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits",
+            "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror",
+            "ulys_last_error")
 
 ULYS_REP_SUFFIX, ULYS_REP_PREFIX, ULYS_REP_KV_PREFIX = 0, 1, 2
 
@@ -219,12 +222,13 @@ def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
 def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                          lse: torch.Tensor | None = None, softmax_scale: float = 0.0, key_gaps=None,
                          key_mask: torch.Tensor | None = None, qk_dtype: int = ULYS_BF16,
-                         qk_amax: torch.Tensor | None = None, stream=None) -> None:
+                         qk_amax: torch.Tensor | None = None, key_splits: int = 0, stream=None) -> None:
     """Attention with q ``[B, Nq, hq, D]`` and k/v ``[B, Nk, hkv, D]`` (Nq may differ from Nk) -> o ``[B, Nq, hq, D]``
     (and lse ``[B, hq, Nq]``).
 
     ``key_mask``: device int32/uint32 words ``[B, ceil(Nk/32)]``, bit ``j % 32`` of word ``j // 32`` set for a
     valid key ``j``, or None (all keys valid).  ``key_gaps`` as for :func:`ulys_attend_group`.
+    ``key_splits``: 0 = automatic (:func:`ulys_attend_splits`), 1 = none, 2..16 = that many key-range runs.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
@@ -248,7 +252,7 @@ def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
             raise ValueError("key_gaps needs one (start, end) per batch")
         gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
     _check(_lib.ulys_attend_group_ex(b, nq, nk, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, mp,
-                                     op, lp, _stream(stream)))
+                                     int(key_splits), op, lp, _stream(stream)))
 
 
 def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_shards, stream=None) -> None:
@@ -316,6 +320,13 @@ def ulys_lse_merge(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tenso
     op = _dev(o_out, "o_out", _BF16, n)
     lp = None if lse_out is None else _dev(lse_out, "lse_out", (torch.float32,), b * heads * rows)
     _check(_lib.ulys_lse_merge(len(o_parts), oa, la, b, rows, heads, d, op, lp, _stream(stream)))
+
+
+def ulys_attend_splits(batch: int, q_rows: int, kv_rows: int, compute_units: int = 256) -> int:
+    """The automatic key-range split (run count) of an attention call of this shape on ``compute_units`` CUs."""
+    st = _lib.ulys_attend_splits(int(batch), int(q_rows), int(kv_rows), int(compute_units))
+    _check(min(st, 0))
+    return st
 
 
 def ulys_auto_groups(layout: Layout, compute_units: int = 256) -> int:
