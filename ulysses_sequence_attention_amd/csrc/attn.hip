@@ -28,15 +28,17 @@
 //    MFMAs of block b+1, which do not depend on them; K operands of b+1 and V
 //    operands of b are read from LDS one phase before their MFMAs.
 //  * Online softmax in the exp2 domain per 32-key block with a lazy max: the
-//    running max is only raised (and O, l rescaled) when some score of a
-//    block exceeds it by more than 8 (a factor 2^8), a wave-uniform branch
-//    taken a few times per row.  The probabilities are formed speculatively
-//    with the current max and redone from the scores (recomputed from K in
-//    LDS) only on that branch, so the check sits after the MFMAs instead of
-//    in front of the exponentials.  Probabilities stay <= 2^8, exact either
-//    way because the final normalisation divides by the sum built with the
-//    same max.  Row sums are fp32 sums of the unrounded probabilities (the
-//    LSE must not inherit the 2^-9 bf16 rounding of the MFMA operand).
+//    probabilities of a block are formed speculatively with the current
+//    running max, and the max is only raised (O, l rescaled, the block's
+//    scores recomputed from K in LDS and its probabilities redone) when a
+//    lane's sum of its 16 probabilities exceeds 2^8 -- which any probability
+//    above 2^8 causes, and which bounds every probability by 2^8 otherwise --
+//    or while the row has no finite max yet.  A wave-uniform branch taken a
+//    few times per row, checked after the MFMAs; no per-block max.  Exact
+//    either way, because the final normalisation divides by the sum built
+//    with the same max.  Row sums are fp32 sums of the unrounded
+//    probabilities (the LSE must not inherit the 2^-9 bf16 rounding of the
+//    MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
 // A head's arithmetic never depends on the other heads of the call, the grid
@@ -69,7 +71,7 @@ constexpr int kBN = kAttnKeysPerTile;        // keys per LDS tile (two 32-key bl
 constexpr int kStages = 3;                   // LDS ring depth (tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;                // raise the running max only past 2^8
+constexpr float kLazySum = 256.0f;           // raise the running max when a lane's block sum exceeds 2^8
 
 template <int D, bool FP8>
 struct Cfg {
@@ -118,8 +120,11 @@ __device__ __forceinline__ float lane_swap_sum(float x) {
 // barrier that publishes a tile.  m0 is set here and used by nothing else.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, unsigned int lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+// The global address is a scalar base plus a 32-bit per-lane offset, so a
+// load needs no vector address arithmetic.
+__device__ __forceinline__ void dma16(const void* sbase, unsigned int voff, unsigned int lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -202,38 +207,63 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- global -> LDS staging of one K/V tile (direct 16-byte loads) ----
   // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i, so each
   // instruction fills one contiguous 1 KB segment; a lane picks the global chunk
-  // that belongs at its LDS position under the XOR swizzle.  Rows past the end
-  // are clamped to the last row (their scores are masked, their V is finite).
+  // that belongs at its LDS position under the XOR swizzle.  The tile's first
+  // row is a scalar base and each lane's byte offset from it is computed once;
+  // in the last tile, when the keys end inside it, rows past the end are
+  // clamped to the last row (their scores are masked, their V is finite) by
+  // offsets of its own.
   const unsigned char* kbase = (const unsigned char*)a.k + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * C::kQKBytes;
   const unsigned char* vbase = (const unsigned char*)a.v + ((size_t)b * rows * kv_row_stride + (size_t)kvh * D) * 2;
+  const unsigned int krow = (unsigned int)(kv_row_stride * C::kQKBytes);   // bytes per key row
+  const unsigned int vrow = (unsigned int)(kv_row_stride * 2);
+  const int last_rows = rows - (ntiles - 1) * kBN;                       // keys in the last tile
+  constexpr int kKRowsPerSeg = 1024 / C::kKRow;
+  constexpr int kVRowsPerSeg = 1024 / C::kVRow;
+  // A wave's u-th load of a tile fetches segment wave + 8u: the same lanes at
+  // 8 kRowsPerSeg more rows (a multiple of the swizzle period), so only its
+  // first offset is per lane and the others move the scalar base.  With fewer
+  // segments than waves (one load each), a surplus wave repeats the last
+  // segment, which keeps every wave's load count per tile the same.
+  static_assert(C::kKSegsPerWave == 1 || C::kKSegs % kWaves == 0, "whole segments per wave");
+  static_assert(C::kVSegsPerWave == 1 || C::kVSegs % kWaves == 0, "whole segments per wave");
+  static_assert((kWaves * kKRowsPerSeg) % C::kKSwz == 0 && (kWaves * kVRowsPerSeg) % 4 == 0, "swizzle period");
+  const int kseg = min(wave, C::kKSegs - 1), vseg = min(wave, C::kVSegs - 1);
+  const int kkey = kseg * kKRowsPerSeg + lane / C::kKChunks;
+  const int kck = (lane % C::kKChunks) ^ (kkey & (C::kKSwz - 1));
+  const unsigned int kgo = kkey * krow + kck * 16;
+  const unsigned int kls = __builtin_amdgcn_readfirstlane(kseg * 1024);
+  const int vkey = vseg * kVRowsPerSeg + lane / C::kVChunks;
+  const int vck = vswz<D>(vkey, 2 * (lane % C::kVChunks)) >> 1;   // global 16-byte chunk of this LDS slot
+  const unsigned int vgo = vkey * vrow + vck * 16;
+  const unsigned int vls = __builtin_amdgcn_readfirstlane(vseg * 1024);
   auto load_tile = [&](int j, auto st) {
-    unsigned char* kl = k_of(st);
-    unsigned char* vl = v_of(st) + kVRegion;
-    const int k0 = j * kBN;
-    constexpr int kKRowsPerSeg = 1024 / C::kKRow;
+    const unsigned int kl = lds_u32(k_of(st)) + kls;
+    const unsigned int vl = lds_u32(v_of(st) + kVRegion) + vls;
+    const size_t k0 = (size_t)j * kBN;
+    const unsigned char* kt = kbase + k0 * krow;
+    const unsigned char* vt = vbase + k0 * vrow;
+    if (j == ntiles - 1 && last_rows < kBN) {
+      // The last tile, when the keys end inside it: rows past the end are
+      // clamped to the last row (their scores are masked, their V is finite).
+      // (lane index laundered so this stays inside the rarely taken branch)
+      int ln;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+      const int kr = kseg * kKRowsPerSeg + ln / C::kKChunks, vr = vseg * kVRowsPerSeg + ln / C::kVChunks;
+      const unsigned int kc = ((ln % C::kKChunks) ^ (kr & (C::kKSwz - 1))) * 16;
+      const unsigned int vc = (vswz<D>(vr, 2 * (ln % C::kVChunks)) >> 1) * 16;
 #pragma unroll
-    for (int u = 0; u < C::kKSegsPerWave; ++u) {
-      // every wave issues the same number of loads (a surplus wave repeats
-      // the last segment), so a wave's outstanding-load count per tile is a
-      // compile-time constant
-      const int seg = min(wave + u * kWaves, C::kKSegs - 1);
-      const int key = seg * kKRowsPerSeg + lane / C::kKChunks;
-      const int sck = lane % C::kKChunks;
-      const int ck = sck ^ (key & (C::kKSwz - 1));
-      const int grow = min(k0 + key, rows - 1);
-      dma16(kbase + (size_t)grow * kv_row_stride * C::kQKBytes + ck * 16,
-            __builtin_amdgcn_readfirstlane(lds_u32(&kl[seg * 1024])));
-    }
-    constexpr int kVRowsPerSeg = 1024 / C::kVRow;
+      for (int u = 0; u < C::kKSegsPerWave; ++u)
+        dma16(kt, min(kr + u * kWaves * kKRowsPerSeg, last_rows - 1) * krow + kc, kl + u * kWaves * 1024);
 #pragma unroll
-    for (int u = 0; u < C::kVSegsPerWave; ++u) {
-      const int seg = min(wave + u * kWaves, C::kVSegs - 1);
-      const int key = seg * kVRowsPerSeg + lane / C::kVChunks;
-      const int sck = lane % C::kVChunks;                 // 16-byte slot in the LDS row
-      const int ck = vswz<D>(key, 2 * sck) >> 1;          // its global 16-byte chunk
-      const int grow = min(k0 + key, rows - 1);
-      dma16(vbase + (size_t)grow * kv_row_stride * 2 + ck * 16,
-            __builtin_amdgcn_readfirstlane(lds_u32(&vl[seg * 1024])));
+      for (int u = 0; u < C::kVSegsPerWave; ++u)
+        dma16(vt, min(vr + u * kWaves * kVRowsPerSeg, last_rows - 1) * vrow + vc, vl + u * kWaves * 1024);
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::kKSegsPerWave; ++u)
+        dma16(kt + u * kWaves * kKRowsPerSeg * krow, kgo, kl + u * kWaves * 1024);
+#pragma unroll
+      for (int u = 0; u < C::kVSegsPerWave; ++u)
+        dma16(vt + u * kWaves * kVRowsPerSeg * vrow, vgo, vl + u * kWaves * 1024);
     }
   };
 
@@ -245,9 +275,12 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m_run = -INFINITY;   // running max of c*log2e*s (lazy)
   float negm = 0.0f;         // -m_run, or 0 while m_run is -inf
-  float thr = -INFINITY;     // raw score above which a block raises m_run: (m_run + 8) / (c log2 e)
+  // A block raises m_run when this lane's sum of its 16 probabilities exceeds
+  // thr: 2^8 (probabilities are >= 0, so a sum <= 2^8 bounds each of them by
+  // 2^8, and a probability above 2^8 makes the sum exceed it), or -1 while
+  // m_run is -inf (every block raises until the row has a finite max).
+  float thr = -1.0f;
   float l_run = 0.0f;        // row sum (this lane's half of the keys)
-  const float inv_c2 = 1.0f / c2;
 
   // Barrier publishing the next tile: this wave's loads of that tile have
   // landed (s_waitcnt vmcnt(N): at most the later tiles' loads still in flight;
@@ -267,17 +300,20 @@ void attn_fwd_kernel(AttnArgs a) {
   // Per-lane LDS byte offsets of the MFMA operand reads, computed once: the
   // XOR swizzles only involve key bits that are the same for every 32-key
   // block, so each read is a base register plus a compile-time offset.
-  //  K (A operand of S^T): lane row l32, head-dim chunk(s) of step kk.
+  //  K (A operand of S^T): lane row l32, head-dim chunk(s) of step kk, in the
+  //  stage the key loop reads next (stage 1 for the first step).  kcur moves
+  //  by one stage per step, so in the loop a K read is this register plus a
+  //  compile-time offset; other stages are reached by a scalar delta.
   constexpr int kKOffs = FP8 ? 2 * C::kQKSteps : C::kQKSteps;
-  int koff[kKOffs];
+  int kcur[kKOffs];
 #pragma unroll
   for (int kk = 0; kk < C::kQKSteps; ++kk) {
     const int sw = l32 & (C::kKSwz - 1);
     if constexpr (!FP8) {
-      koff[kk] = l32 * C::kKRow + (((kk * 2 + hh) ^ sw) * 16);
+      kcur[kk] = C::kKTile + l32 * C::kKRow + (((kk * 2 + hh) ^ sw) * 16);
     } else {
-      koff[2 * kk] = l32 * C::kKRow + (((kk * 4 + hh * 2) ^ sw) * 16);
-      koff[2 * kk + 1] = l32 * C::kKRow + (((kk * 4 + hh * 2 + 1) ^ sw) * 16);
+      kcur[2 * kk] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2) ^ sw) * 16);
+      kcur[2 * kk + 1] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2 + 1) ^ sw) * 16);
     }
   }
   //  V (A operand of O^T, transposing reads): within 16 lanes, lane 4j+t reads
@@ -295,12 +331,30 @@ void attn_fwd_kernel(AttnArgs a) {
   struct KFrag { u32x4 x[kKOffs]; };      // K operands of one 32-key block
   struct VFrag { bf16x8 x[C::kDB][2]; };  // V^T operands of one 32-key block
 
-  auto read_k = [&](const unsigned char* kl, auto kb, KFrag& kf) ULYS_INLINE {
-    const unsigned char* kblk = kl + int(kb) * 32 * C::kKRow;
+  // K operands of block kb of the stage `delta` bytes from kcur's (one, or all).
+  auto read_k_one = [&](int delta, auto kb, int i, KFrag& kf) ULYS_INLINE {
+    kf.x[i] = *(const u32x4*)(lds + kcur[i] + delta + int(kb) * 32 * C::kKRow);
+  };
+  auto read_k = [&](int delta, auto kb, KFrag& kf) ULYS_INLINE {
 #pragma unroll
-    for (int i = 0; i < kKOffs; ++i) kf.x[i] = *(const u32x4*)(kblk + koff[i]);
+    for (int i = 0; i < kKOffs; ++i) read_k_one(delta, kb, i, kf);
   };
 
+  // One head-dim step kk of S^T = K Q^T.
+  auto qk_step = [&](const KFrag& kf, int kk, f32x16 s) ULYS_INLINE {
+    if constexpr (!FP8) {
+      const u32x4 qx = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[kk]),
+                                                     __builtin_bit_cast(bf16x8, qx), s, 0, 0, 0);
+    } else {
+      const u32x4 k0x = kf.x[2 * kk], k1x = kf.x[2 * kk + 1];
+      const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
+                        (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
+      const i32x8 bq = {(int)qf[kk][0], (int)qf[kk][1], (int)qf[kk][2], (int)qf[kk][3],
+                        (int)qf[kk][4], (int)qf[kk][5], (int)qf[kk][6], (int)qf[kk][7]};
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s, 0, 0, 0, 127, 0, 127);
+    }
+  };
   // S^T = K Q^T for one 32-key block.
   auto qk = [&](const KFrag& kf) ULYS_INLINE {
     f32x16 s;
@@ -327,18 +381,19 @@ void attn_fwd_kernel(AttnArgs a) {
   // V^T operands of one 32-key block: lane l needs V[key(hh, i)][d = 32 db + l%32],
   // i = 0..7, read as two transposing 8-byte loads over keys base + 4 hh + (0..3)
   // and base + 8 + 4 hh + (0..3) -- the keys whose probabilities p[e] holds.
+  auto read_v_one = [&](const unsigned char* vl, auto kb, int db, int e, VFrag& vf) ULYS_INLINE {
+    const unsigned char* va_p = vl + (int(kb) * 32 + 16 * e) * C::kVRow + voff[db];
+    const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
+    const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
+    vf.x[db][e] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
   auto read_v = [&](const unsigned char* vl, auto kb, VFrag& vf) ULYS_INLINE {
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const unsigned char* va_p = vl + (int(kb) * 32 + 16 * e) * C::kVRow + voff[db];
-        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p));
-        const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(unsigned char*)(va_p + 8 * C::kVRow));
-        vf.x[db][e] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int e = 0; e < 2; ++e) read_v_one(vl, kb, db, e, vf);
   };
 
   // O^T += V^T P^T for one 32-key block.
@@ -396,17 +451,18 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Probabilities exp2(c log2e s - m_run) of accumulator registers 8e..8e+7
   // -> bf16 B operand p[e] of the PV MFMA, and their fp32 sums in two chains.
+  auto probs_pair = [&](const f32x16& s, int e, int i, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, negm));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, negm));
+    const f32x2 xx = {x0, x1};
+    const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
+    p[e][2 * i] = pk[0];
+    p[e][2 * i + 1] = pk[1];
+    if (e == 0 && i == 0) { ls0 = x0; ls1 = x1; } else { ls0 += x0; ls1 += x1; }
+  };
   auto probs_half = [&](const f32x16& s, int e, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, negm));
-      const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, negm));
-      const f32x2 xx = {x0, x1};
-      const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
-      p[e][2 * i] = pk[0];
-      p[e][2 * i + 1] = pk[1];
-      if (e == 0 && i == 0) { ls0 = x0; ls1 = x1; } else { ls0 += x0; ls1 += x1; }
-    }
+    for (int i = 0; i < 4; ++i) probs_pair(s, e, i, p, ls0, ls1);
   };
   auto probs = [&](const f32x16& s, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
     probs_half(s, 0, p, ls0, ls1);
@@ -423,25 +479,26 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Raising the running max (rare: a few times per row).  The PV MFMAs of the
   // previous block were formed with the old max and are already accumulated,
-  // so O and l are rescaled by exp2(m_old - m_new); then this block's scores
-  // are recomputed from K in LDS and its probabilities redone with the new max.
-  auto raise_max = [&](float pm, const unsigned char* kl, int kb, int kb0, unsigned mword, bf16x8 (&p)[2],
-                       float& ls0, float& ls1) ULYS_INLINE {
-    const float mx = lane_swap_max(pm) * c2;
+  // so O and l are rescaled by exp2(m_old - m_new); this block's scores are
+  // recomputed from K in LDS, their max taken, and the probabilities redone
+  // with the new max.
+  auto raise_max = [&](int kdelta, int kb, int kb0, unsigned mword, bf16x8 (&p)[2], float& ls0,
+                       float& ls1) ULYS_INLINE {
+    KFrag kf;
+    read_k(kdelta, kb, kf);
+    f32x16 s = qk(kf);
+    mask(s, kb0, mword);
+    const float mx = lane_swap_max(part_max(s)) * c2;
     const float mn = fmaxf(m_run, mx);
     const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
     m_run = mn;
     negm = (mn == -INFINITY) ? 0.0f : -mn;
-    thr = (mn == -INFINITY) ? -INFINITY : (mn + kLazy) * inv_c2;
+    thr = (mn == -INFINITY) ? -1.0f : kLazySum;
     l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    KFrag kf;
-    read_k(kl, kb, kf);
-    f32x16 s = qk(kf);
-    mask(s, kb0, mword);
     probs(s, p, ls0, ls1);
   };
 
@@ -483,30 +540,45 @@ void attn_fwd_kernel(AttnArgs a) {
   // s_out = S(b+1) (K of stage st_next, block kb_next), p_out = P(b), and
   // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b,
   // mword = its key-mask word.
-  auto iteration = [&](auto st_next, auto kb_next, auto st, auto kb, int kb0, unsigned mword, f32x16& s_in,
+  auto iteration = [&](auto read_next, auto st, int kdelta, auto kb, int kb0, unsigned mword, f32x16& s_in,
                        f32x16& s_out, bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
     mask(s_in, kb0, mword);
-    // phase 1: K reads of block b+1; PV(b-1) MFMAs under the row max and the
-    // first half of the probabilities of block b
     KFrag kf;
-    read_k(k_of(st_next), kb_next, kf);
-    const float pm = part_max(s_in);
     float ls0, ls1;
-    probs_half(s_in, 0, p_out, ls0, ls1);
-    pv(vf, p_in);
-    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, kPVMfma>{},
-               std::integral_constant<int, 0>{}, std::integral_constant<int, (8 + 26 + kPVMfma - 1) / kPVMfma>{});
-    __builtin_amdgcn_sched_barrier(0);
-    // phase 2: V reads of block b (into the registers PV(b-1) just consumed);
-    // QK(b+1) MFMAs under the second half of the probabilities
-    read_v(v_of(st), kb, vf);
-    s_out = qk(kf);
-    probs_half(s_in, 1, p_out, ls0, ls1);
-    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, kQKMfma>{},
-               std::integral_constant<int, (kVReads + kQKMfma - 1) / kQKMfma>{},
-               std::integral_constant<int, (29 + kQKMfma - 1) / kQKMfma>{});
+    // Explicit issue order, one MFMA per group (the scheduler may not move
+    // work across a group boundary), so each MFMA has independent vector and
+    // LDS work issued beside it.
+    // phase 1: PV(b-1) MFMAs, each with its share of the K reads of block b+1
+    // and of the first half of the probabilities of block b
+#pragma unroll
+    for (int g = 0; g < kPVMfma; ++g) {
+      const int db = g % C::kDB, e = g / C::kDB;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.x[db][e], p_in[e], o[db], 0, 0, 0);
+#pragma unroll
+      for (int i = g * kKOffs / kPVMfma; i < (g + 1) * kKOffs / kPVMfma; ++i) read_next(i, kf);
+#pragma unroll
+      for (int i = g * 4 / kPVMfma; i < (g + 1) * 4 / kPVMfma; ++i) probs_pair(s_in, 0, i, p_out, ls0, ls1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 2: QK(b+1) MFMAs, each with its share of the V reads of block b
+    // (into the registers PV(b-1) consumed) and of the second half of the
+    // probabilities
+    f32x16 sn;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[r] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kQKMfma; ++g) {
+      sn = qk_step(kf, g, sn);
+#pragma unroll
+      for (int j = g * (2 * C::kDB) / kQKMfma; j < (g + 1) * (2 * C::kDB) / kQKMfma; ++j)
+        read_v_one(v_of(st), kb, j % C::kDB, j / C::kDB, vf);
+#pragma unroll
+      for (int i = g * 4 / kQKMfma; i < (g + 1) * 4 / kQKMfma; ++i) probs_pair(s_in, 1, i, p_out, ls0, ls1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_out = sn;
     pin(p_out, ls0, ls1);
-    if (__any(pm > thr)) raise_max(pm, k_of(st), kb, kb0, mword, p_out, ls0, ls1);
+    if (__any(ls0 + ls1 > thr)) raise_max(kdelta, kb, kb0, mword, p_out, ls0, ls1);
     l_run += ls0 + ls1;
   };
 
@@ -565,7 +637,7 @@ void attn_fwd_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
     {
       KFrag kf;
-      read_k(k_of(B0{}), B0{}, kf);
+      read_k(-C::kKTile, B0{}, kf);
       sA = qk(kf);
       read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
     }
@@ -573,7 +645,9 @@ void attn_fwd_kernel(AttnArgs a) {
     // mask words of the tile's second block (mw1) and of the next tile's blocks
     // (fetched a block ahead: each is a scalar value once it is used)
     unsigned mw1 = mask_word(tc * kBN + 32);
-    iteration(B0{}, B1{}, B0{}, B0{}, tc * kBN, __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), sA, sB, pA, pB);
+    iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
+              tc * kBN,
+              __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), sA, sB, pA, pB);
     tile_barrier();
 
     // Position i (stage SA): its second block, then the first block of
@@ -585,11 +659,18 @@ void attn_fwd_kernel(AttnArgs a) {
       load_pos(i + kStages - 1, SP);
       const int tn = i + 1 < n ? seq_tile(i + 1) : tc;
       const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
-      iteration(SB, B0{}, SA, B1{}, tc * kBN + 32, __builtin_amdgcn_readfirstlane(mw1), sB, sA, pB, pA);
+      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
+                tc * kBN + 32,
+                __builtin_amdgcn_readfirstlane(mw1), sB, sA, pB, pA);
       if (i + 1 >= n) return false;
       tc = tn;
       mw1 = wn1;
-      iteration(SB, B1{}, SB, B0{}, tc * kBN, __builtin_amdgcn_readfirstlane(wn0), sA, sB, pA, pB);
+      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
+                __builtin_amdgcn_readfirstlane(wn0), sA, sB, pA, pB);
+      // the next step reads K from the stage after SB
+      const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
+#pragma unroll
+      for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
       tile_barrier();
       return true;
     };
