@@ -128,35 +128,41 @@ def device_copy_gbs(torch) -> float:
 
 
 def group_sweep():
-    """One JSON line per sequence length: attention time of 10 heads split into G calls, and the
-    group count ulys_auto_groups picks for that shape (Wan-like layout, Ulysses degree 4)."""
+    """One JSON line per sequence length: attention time of 10 heads split into G calls (with the
+    automatic key-range split, and with none), the split count and the group count ulys_auto_groups
+    picks for that shape (Wan-like layout, Ulysses degree 4)."""
     import torch
     from ulysses_sequence_attention_amd import ulys
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     gen = torch.Generator(device="cpu").manual_seed(0)
     for rows in (2048, 4096, 8192, 16384, 27280):
-        times = {}
-        for gh in (10, 5, 2, 1):
-            G = 10 // gh
-            q = torch.randn((G, 1, rows, gh, 128), generator=gen).to(torch.bfloat16).cuda()
-            k, v = q.roll(1, dims=2), q.roll(2, dims=2)
-            o = torch.empty_like(q)
-            lse = torch.empty((G, 1, gh, rows), device="cuda")
-            run = lambda: [ulys.ulys_attend_group(q[g], k[g], v[g], o[g], lse[g]) for g in range(G)]
-            for _ in range(3):
-                run()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            times[G] = e0.elapsed_time(e1) / 10
+        times = {0: {}, 1: {}}
+        for splits in (0, 1):
+            for gh in (10, 5, 2, 1):
+                G = 10 // gh
+                q = torch.randn((G, 1, rows, gh, 128), generator=gen).to(torch.bfloat16).cuda()
+                k, v = q.roll(1, dims=2), q.roll(2, dims=2)
+                o = torch.empty_like(q)
+                lse = torch.empty((G, 1, gh, rows), device="cuda")
+                run = lambda: [ulys.ulys_attend_group_ex(q[g], k[g], v[g], o[g], lse[g], key_splits=splits)
+                               for g in range(G)]
+                for _ in range(3):
+                    run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                times[splits][G] = e0.elapsed_time(e1) / 10
+        t = times[0]
         L = ulys.Layout(1, 4, rows // 4, 0, True, 40, 40, 128, 1)
         print(json.dumps({"rows": rows, "heads": 10, "cus": cus,
-                          "ms_by_groups": {str(G): round(t, 4) for G, t in sorted(times.items())},
-                          "relative_to_one_call": {str(G): round(t / times[1], 3) for G, t in sorted(times.items())},
+                          "key_splits": ulys.ulys_attend_splits(1, rows, rows, cus),
+                          "ms_by_groups": {str(G): round(x, 4) for G, x in sorted(t.items())},
+                          "relative_to_one_call": {str(G): round(x / t[1], 3) for G, x in sorted(t.items())},
+                          "ms_by_groups_unsplit": {str(G): round(x, 4) for G, x in sorted(times[1].items())},
                           "auto_groups": ulys.ulys_auto_groups(L, cus)}), flush=True)
 
 

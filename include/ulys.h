@@ -182,7 +182,9 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
  * compute_units workgroups and a partial round costs nearly a full one): G is
  * accepted when G calls take no more rounds than the one call over all the
  * rank's heads, i.e. G * ceil(W / G / cus) <= ceil(W / cus) with
- * W = batch * (Hq/P) * ceil(rows_q / 256).  Returns the count (>= 1; 1 = keep
+ * W = batch * (Hq/P) * ceil(rows_q / 256) * C, C the automatic key-range
+ * split of the shape (ulys_attend_splits; it does not depend on the head
+ * count, so it is the same for every G).  Returns the count (>= 1; 1 = keep
  * the sequential single call); layout->groups is ignored.
  * Rules: the layout rules with groups = 1; compute_units >= 1 (ULYS_EINVAL).
  */

@@ -230,20 +230,24 @@ def _groups(U, **kw):
 
 
 def test_auto_groups_follow_the_rounds_rule(U):
-    """Wan2.1 at Ulysses 4 (27280 rows, 10 heads per rank): one call takes ceil(1070/256) = 5
-    rounds of workgroups, five 2-head calls 5 x 1 -> 5 groups.  Measured on MI355X (group-split
-    sweep): 16384 rows (3 rounds) gets no split, 8192 rows (2 rounds) splits in two."""
+    """Wan2.1 at Ulysses 4 (27280 rows, 10 heads per rank, no key-range split): one call takes
+    ceil(1070/256) = 5 rounds of workgroups, five 2-head calls 5 x 1 -> 5 groups.  With the key-range
+    split (2 runs below 27280 rows) the workgroups double.  Measured on MI355X (group-split sweep):
+    16384 rows: one call 5 rounds, five calls 5 x 1 (1.358 vs 1.350 ms) -> 5; 8192 rows: one call
+    3 rounds, two calls 2 x 2 (0.491 vs 0.430 ms) -> 1; 4096 rows: 2 rounds either way -> 2."""
     assert _groups(U) == 5
-    assert _groups(U, s_local=16384 // 4) == 1
-    assert _groups(U, s_local=8192 // 4) == 2
-    assert _groups(U, s_local=1024) == 1                               # small image: one call
+    assert _groups(U, s_local=16384 // 4) == 5
+    assert _groups(U, s_local=8192 // 4) == 1
+    assert _groups(U, s_local=4096 // 4) == 2
+    assert _groups(U, s_local=2048 // 4) == 1                          # 8 x 10 x 2 = 160 workgroups: one call
     assert _groups(U, groups=3) == 5                                   # the layout's own count is ignored
-    # 12 heads per rank, 32760 rows: W = 12 x 128 = 1536 -> 6 rounds; 7 and 5 do not divide 12,
-    # 4 groups take 4 x 2 = 8 rounds, 3 groups 3 x 2 = 6
+    # 12 heads per rank, 32760 rows (no key split): W = 12 x 128 = 1536 -> 6 rounds; 7 and 5 do not
+    # divide 12, 4 groups take 4 x 2 = 8 rounds, 3 groups 3 x 2 = 6
     assert _groups(U, hq=48, hkv=48, s_local=8190) == 3
-    # GQA 40/8 at P 4: only 2 divides the 2 k/v heads per rank, and 2 x 3 rounds > 5
+    # GQA 40/8 at P 4: only 2 divides the 2 k/v heads per rank; 2 x 3 rounds > 5, and at 8192 rows
+    # (2 key runs) 2 x 2 > 3
     assert _groups(U, hq=40, hkv=8) == 1
-    assert _groups(U, hq=40, hkv=8, s_local=8192 // 4) == 2
+    assert _groups(U, hq=40, hkv=8, s_local=8192 // 4) == 1
     assert U.call_raw("ulys_auto_groups", None, 256) == -1
     c = U.Layout(**dict(GOOD)).c_struct()
     assert U.call_raw("ulys_auto_groups", ctypes.byref(c), 0) == -1

@@ -501,13 +501,16 @@ int ulys_auto_groups(const ulys_layout* L, int compute_units) {
   const int st = check_layout(&one, 0, -1);
   if (st) return st;
   // query rows of one call (a K/V-only prefix adds keys, not query rows)
+  const long long rows_kv = (long long)L->n_rep + (long long)L->degree * L->s_local;
   const long long rows = (L->rep_first == ULYS_REP_KV_PREFIX ? 0LL : (long long)L->n_rep) +
                          (long long)L->degree * L->s_local;
   const long long hq_rank = L->hq / L->degree, hkv_rank = L->hkv / L->degree;
-  // Workgroups of the one-call attention (256 query rows each, one per CU at
-  // a time) and the rounds of CUs they take.
-  const long long wgs = (long long)L->batch * hq_rank * ((rows + ulys::kAttnRowsPerWorkgroup - 1) /
-                                                        ulys::kAttnRowsPerWorkgroup);
+  // Workgroups of the one-call attention (256 query rows each, times the
+  // automatic key-range split, which is the same for every group count; one
+  // per CU at a time) and the rounds of CUs they take.
+  const long long splits = auto_splits(L->batch, rows, rows_kv, compute_units);
+  const long long wgs = (long long)L->batch * hq_rank * splits *
+                        ((rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup);
   const long long rounds_one = (wgs + compute_units - 1) / compute_units;
   static const int kCandidates[] = {7, 5, 4, 3, 2};
   for (int G : kCandidates) {
