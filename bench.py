@@ -86,6 +86,35 @@ def measured_traffic(groups: int):
     return entry["hbm_bytes_per_launch"]
 
 
+def fp8_attention(torch, ulys, L, shards, qs, os_, lse, flops_launch: float, steps: int) -> dict:
+    """The same attention launches with e4m3 q/k: amax over the shards, the fp8 pack of rank 0's
+    slots, then `steps` timed rounds of the G launches (HIP events).  Reported beside the bf16
+    figure; the headline stays bf16."""
+    amax = torch.zeros(2, dtype=torch.float32, device=qs.device)
+    ulys.ulys_amax_bf16(shards["q"], amax[0:1])
+    ulys.ulys_amax_bf16(shards["k"], amax[1:2])
+    q8 = torch.empty(qs.shape, dtype=torch.uint8, device=qs.device)
+    k8 = torch.empty_like(q8)
+    v16 = torch.empty_like(qs)
+    ulys.ulys_pack(L, 0, -1, shards["q"], shards["k"], shards["v"], q8, k8, v16,
+                   qk_dtype=ulys.ULYS_FP8_E4M3, qk_amax=amax)
+    G = qs.shape[0]
+    run = lambda: [ulys.ulys_attend_group(q8[g], k8[g], v16[g], os_[g], lse[g], qk_dtype=ulys.ULYS_FP8_E4M3,
+                                          qk_amax=amax) for g in range(G)]
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps / G
+    return {"launch_ms": round(ms, 4), "tflops_bf16_equivalent": round(flops_launch / (ms * 1e-3) / 1e12, 2),
+            "note": "e4m3 q/k (QK^T at the fp8 MFMA rate), bf16 V and P; FLOPs counted as for bf16"}
+
+
 def merge_gbs(torch, ulys, o_slots, lse, steps: int) -> float:
     """ulys_lse_merge of the G head-group outputs taken as G partial results of one slot shape
     (a ring of G): algorithmic bytes (G partial o + lse read, one o + lse written) over the mean
@@ -415,6 +444,7 @@ def main():
                      "traffic": measured_traffic(G), "kernel": ATTN_KERNEL,
                      "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
     }
+    res["attention_fp8_qk"] = fp8_attention(torch, ulys, L, shards, qs, os_, lse, flops_step / G, args.steps)
     res["lse_merge_gbs"] = round(merge_gbs(torch, ulys, os_, lse, args.steps), 1)
     res["hbm_copy_gbs"] = round(device_copy_gbs(torch), 1)
     if not args.no_cpu_baseline:
