@@ -237,9 +237,10 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * combines them in run order with the log-sum-exp weights.  C depends on
  * (batch, rows, the device's compute units) only, so the head-subset rule
  * above still holds.  The partials live in a device workspace that the
- * library allocates per (device, stream) on first use and keeps (at most
- * 2 GiB; a call needing more runs its heads in several launches); calls on
- * one stream share it in stream order.
+ * library allocates per (device, stream) on first use and keeps (up to
+ * 2 GiB, or one head's partials when those alone need more; a call needing
+ * more runs its heads in several launches); calls on one stream share it in
+ * stream order.
  */
 int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       const void* q, const void* k, const void* v, int qk_dtype,
