@@ -46,6 +46,8 @@ SPLIT_CASES = [  # b, nq, nk, hq, hkv, d, splits, gaps
     (1, 200, 200, 2, 2, 128, 16, None),          # 4 key tiles: 12 runs are empty
     (3, 100, 1000, 4, 4, 64, 16, None),          # 16 tiles: one per run
     (1, 1030, 3333, 2, 2, 128, 5, [(3300, 3333)]),
+    (1, 1, 4100, 1, 1, 128, 4, None),            # one query row
+    (2, 33, 65, 2, 2, 64, 2, None),              # two tiles, the second holding one key
 ]
 
 
