@@ -236,13 +236,19 @@ void attn_fwd_kernel(AttnArgs a) {
   const int vck = vswz<D>(vkey, 2 * (lane % C::kVChunks)) >> 1;   // global 16-byte chunk of this LDS slot
   const unsigned int vgo = vkey * vrow + vck * 16;
   const unsigned int vls = __builtin_amdgcn_readfirstlane(vseg * 1024);
+  const unsigned int ktile = kBN * krow, vtile = kBN * vrow;   // bytes per tile (hq <= 65535: fits)
+  const int tail_tile = last_rows < kBN ? ntiles - 1 : -1;
+  unsigned int kgo_u[C::kKSegsPerWave], vgo_u[C::kVSegsPerWave];
+#pragma unroll
+  for (int u = 0; u < C::kKSegsPerWave; ++u) kgo_u[u] = kgo + u * kWaves * kKRowsPerSeg * krow;
+#pragma unroll
+  for (int u = 0; u < C::kVSegsPerWave; ++u) vgo_u[u] = vgo + u * kWaves * kVRowsPerSeg * vrow;
   auto load_tile = [&](int j, auto st) {
     const unsigned int kl = lds_u32(k_of(st)) + kls;
     const unsigned int vl = lds_u32(v_of(st) + kVRegion) + vls;
-    const size_t k0 = (size_t)j * kBN;
-    const unsigned char* kt = kbase + k0 * krow;
-    const unsigned char* vt = vbase + k0 * vrow;
-    if (j == ntiles - 1 && last_rows < kBN) {
+    const unsigned char* kt = kbase + (size_t)(unsigned int)j * ktile;
+    const unsigned char* vt = vbase + (size_t)(unsigned int)j * vtile;
+    if (j == tail_tile) {
       // The last tile, when the keys end inside it: rows past the end are
       // clamped to the last row (their scores are masked, their V is finite).
       // (lane index laundered so this stays inside the rarely taken branch)
@@ -259,11 +265,9 @@ void attn_fwd_kernel(AttnArgs a) {
         dma16(vt, min(vr + u * kWaves * kVRowsPerSeg, last_rows - 1) * vrow + vc, vl + u * kWaves * 1024);
     } else {
 #pragma unroll
-      for (int u = 0; u < C::kKSegsPerWave; ++u)
-        dma16(kt + u * kWaves * kKRowsPerSeg * krow, kgo, kl + u * kWaves * 1024);
+      for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(kt, kgo_u[u], kl + u * kWaves * 1024);
 #pragma unroll
-      for (int u = 0; u < C::kVSegsPerWave; ++u)
-        dma16(vt + u * kWaves * kVRowsPerSeg * vrow, vgo, vl + u * kWaves * 1024);
+      for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vt, vgo_u[u], vl + u * kWaves * 1024);
     }
   };
 
@@ -429,9 +433,11 @@ void attn_fwd_kernel(AttnArgs a) {
   // Invalid keys of the block from kb0 -> -inf: selects under one wave-uniform
   // branch, taken for blocks that straddle the end or the gap, or whose mask
   // word (uniform, scalar) is not all ones (the key of register r is
-  // kb0 + 8 (r/4) + 4 hh + r%4).
-  auto mask = [&](f32x16& s, int kb0, unsigned mword) ULYS_INLINE {
-    if (straddles(kb0) || (MASK && mword != ~0u)) {
+  // kb0 + 8 (r/4) + 4 hh + r%4).  The range test runs only in tiles flagged
+  // dirty (at most three per row of tiles), which keeps it off the scalar
+  // unit in every other tile.
+  auto mask = [&](f32x16& s, int kb0, unsigned mword, bool dirty) ULYS_INLINE {
+    if ((dirty && straddles(kb0)) || (MASK && mword != ~0u)) {
       const unsigned vbits = __builtin_amdgcn_readfirstlane(valid_bits(kb0, mword));
       // (volatile: keeps this lane-dependent work inside the rarely taken branch)
       unsigned lb;
@@ -482,12 +488,12 @@ void attn_fwd_kernel(AttnArgs a) {
   // so O and l are rescaled by exp2(m_old - m_new); this block's scores are
   // recomputed from K in LDS, their max taken, and the probabilities redone
   // with the new max.
-  auto raise_max = [&](int kdelta, int kb, int kb0, unsigned mword, bf16x8 (&p)[2], float& ls0,
+  auto raise_max = [&](int kdelta, int kb, int kb0, unsigned mword, bool dirty, bf16x8 (&p)[2], float& ls0,
                        float& ls1) ULYS_INLINE {
     KFrag kf;
     read_k(kdelta, kb, kf);
     f32x16 s = qk(kf);
-    mask(s, kb0, mword);
+    mask(s, kb0, mword, dirty);
     const float mx = lane_swap_max(part_max(s)) * c2;
     const float mn = fmaxf(m_run, mx);
     const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
@@ -526,9 +532,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // s_out = S(b+1) (K of stage st_next, block kb_next), p_out = P(b), and
   // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b,
   // mword = its key-mask word.
-  auto iteration = [&](auto read_next, auto st, int kdelta, auto kb, int kb0, unsigned mword, f32x16& s_in,
-                       f32x16& s_out, bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
-    mask(s_in, kb0, mword);
+  auto iteration = [&](auto read_next, auto st, int kdelta, auto kb, int kb0, unsigned mword, bool dirty,
+                       f32x16& s_in, f32x16& s_out, bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
+    mask(s_in, kb0, mword, dirty);
     KFrag kf;
     float ls0, ls1;
     // phase 1: PV(b-1) MFMAs in explicit issue groups (the scheduler may not
@@ -571,7 +577,7 @@ void attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(1);
     s_out = sn;
     pin(p_out, ls0, ls1);
-    if (__any(ls0 + ls1 > thr)) raise_max(kdelta, kb, kb0, mword, p_out, ls0, ls1);
+    if (__any(ls0 + ls1 > thr)) raise_max(kdelta, kb, kb0, mword, dirty, p_out, ls0, ls1);
     l_run += ls0 + ls1;
   };
 
@@ -635,12 +641,24 @@ void attn_fwd_kernel(AttnArgs a) {
       read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
     }
     int tc = seq_tile(0);
+    // Tiles with keys outside [0, rows) or inside the gap: the one holding the
+    // gap's first key, the one holding its last, and the ragged last tile
+    // (ascending; tiles are visited in ascending order, so one compare per
+    // tile against the next of them decides whether its blocks take the
+    // per-block range test).
+    constexpr int kNone = 0x7fffffff;
+    const int dz = tail_tile >= 0 ? tail_tile : kNone;
+    const int dx = gs < ge ? gs / kBN : dz, dy = gs < ge ? (ge - 1) / kBN : dz;
+    auto next_dirty = [&](int t) { return dx > t ? dx : dy > t ? dy : dz > t ? dz : kNone; };
+    int nd = next_dirty(tc - 1);
+    bool dc = tc == nd;
+    if (dc) nd = next_dirty(tc);
     // mask words of the tile's second block (mw1) and of the next tile's blocks
     // (fetched a block ahead: each is a scalar value once it is used)
     unsigned mw1 = mask_word(tc * kBN + 32);
     iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
               tc * kBN,
-              __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), sA, sB, pA, pB);
+              __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), dc, sA, sB, pA, pB);
     tile_barrier();
 
     // Position i (stage SA): its second block, then the first block of
@@ -654,12 +672,14 @@ void attn_fwd_kernel(AttnArgs a) {
       const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
       iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
                 tc * kBN + 32,
-                __builtin_amdgcn_readfirstlane(mw1), sB, sA, pB, pA);
+                __builtin_amdgcn_readfirstlane(mw1), dc, sB, sA, pB, pA);
       if (i + 1 >= n) return false;
       tc = tn;
       mw1 = wn1;
+      dc = tc == nd;
+      if (dc) nd = next_dirty(tc);
       iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
-                __builtin_amdgcn_readfirstlane(wn0), sA, sB, pA, pB);
+                __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
       // the next step reads K from the stage after SB
       const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
 #pragma unroll
