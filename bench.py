@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 ATTN_KERNEL = "attn_fwd_kernel<128, false, false>"   # D = 128, bf16 q/k, no key mask
+MERGE_KERNEL = "range_merge_kernel<128>"             # the range split's merge, when the call uses one
 
 
 def parse():
@@ -158,8 +159,8 @@ def device_copy_gbs(torch) -> float:
 
 def group_sweep():
     """One JSON line per sequence length: attention time of 10 heads split into G calls (with the
-    automatic key-range split, and with none), the split count and the group count ulys_auto_groups
-    picks for that shape (Wan-like layout, Ulysses degree 4)."""
+    automatic key-range or range split, and with none), the split counts and the group count
+    ulys_auto_groups picks for that shape (Wan-like layout, Ulysses degree 4)."""
     import torch
     from ulysses_sequence_attention_amd import ulys
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -189,6 +190,7 @@ def group_sweep():
         L = ulys.Layout(1, 4, rows // 4, 0, True, 40, 40, 128, 1)
         print(json.dumps({"rows": rows, "heads": 10, "cus": cus,
                           "key_splits": ulys.ulys_attend_splits(1, rows, rows, cus),
+                          "range_split": ulys.ulys_attend_ranges(1, rows, rows, cus),
                           "ms_by_groups": {str(G): round(x, 4) for G, x in sorted(t.items())},
                           "relative_to_one_call": {str(G): round(x / t[1], 3) for G, x in sorted(t.items())},
                           "ms_by_groups_unsplit": {str(G): round(x, 4) for G, x in sorted(times[1].items())},
@@ -248,7 +250,7 @@ def summarize_profiles(d: str):
     wcopy, _ = counter("write_copy", "WRITE_SIZE", "copyBuffer")
     n = 1 << 30
     fscale, wscale = n / (fcopy * 1024), n / (wcopy * 1024)
-    out = {"kernel": attn,
+    out = {"kernel": attn + " + range_merge_kernel<128> (when the launch takes a range split)",
            "workload": "Wan2.1 Ulysses-4 share: q/k/v slots [1,27280,10/G,128] bf16, non-causal, LSE",
            "source_sha256": kernel_source_hash(),
            "calibration": {"copy": f"__amd_rocclr_copyBuffer of 1 GiB (torch copy_), {ncopy} dispatches",
@@ -266,6 +268,14 @@ def summarize_profiles(d: str):
         heads = 10 // G
         f, _ = counter(f"fetch_g{G}", "FETCH_SIZE", attn)
         w_, _ = counter(f"write_g{G}", "WRITE_SIZE", attn)
+        try:   # the range split's merge belongs to the launch
+            fm, _ = counter(f"fetch_g{G}", "FETCH_SIZE", "range_merge_kernel<128>")
+            wm, _ = counter(f"write_g{G}", "WRITE_SIZE", "range_merge_kernel<128>")
+        except SystemExit:
+            fm = wm = 0.0
+        print(f"| `range_merge_kernel<128>` | {G} | {fm:.1f} | {wm:.1f} | {fm * 1024 * fscale:.4g} | "
+              f"{wm * 1024 * wscale:.4g} | | |")
+        f, w_ = f + fm, w_ + wm
         rd, wr = f * 1024 * fscale, w_ * 1024 * wscale
         alg_r = 3 * rows * heads * 128 * 2
         alg_w = rows * heads * 128 * 2 + rows * heads * 4
@@ -274,8 +284,8 @@ def summarize_profiles(d: str):
                                      "hbm_write_bytes": int(wr), "hbm_bytes_per_launch": int(rd + wr),
                                      "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
                                      "read_over_algorithmic": round(rd / alg_r, 2)}
-        print(f"| `{attn}` | {G} | {f:.1f} | {w_:.1f} | {rd:.4g} | {wr:.4g} | {alg_r:.4g} / {alg_w:.4g} | "
-              f"{rd / alg_r:.2f} |")
+        print(f"| launch (`{attn}` + merge) | {G} | {f:.1f} | {w_:.1f} | {rd:.4g} | {wr:.4g} | "
+              f"{alg_r:.4g} / {alg_w:.4g} | {rd / alg_r:.2f} |")
         for kname, alg in (("pack_kernel", None), ("unpack_kernel", None)):
             try:
                 fk, nk = counter(f"fetch_g{G}", "FETCH_SIZE", kname)
@@ -406,6 +416,10 @@ def main():
     attn_ms = sum(r["p1"].elapsed_time(r["a1"]) for r in recs) / args.steps
     unpack_ms = sum(r["a1"].elapsed_time(r["u1"]) for r in recs) / args.steps
     attn_launch_ms = attn_ms / G
+    # an attention launch is the attention kernel plus, under the automatic range split, its merge
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ranges = ulys.ulys_attend_ranges(1, rows, rows, cus)
+    launch_kernels = ATTN_KERNEL + (f" + {MERGE_KERNEL}" if ranges > 0 else "")
     attn_tflops = flops_step / (attn_ms * 1e-3) / 1e12
     value = flops_step / (ms_step * 1e-3) / 1e12
     repack_gbs = (bytes_pack + bytes_unpack) / ((pack_ms + unpack_ms) * 1e-3) / 1e9
@@ -441,8 +455,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops_step / G / (attn_launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(G), "kernel": ATTN_KERNEL,
-                     "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G},
+                     "traffic": measured_traffic(G), "kernel": launch_kernels,
+                     "launch_ms": round(attn_launch_ms, 4), "flops_per_launch": flops_step / G,
+                     "range_split": ranges},
     }
     res["attention_fp8_qk"] = fp8_attention(torch, ulys, L, shards, qs, os_, lse, flops_step / G, args.steps)
     res["lse_merge_gbs"] = round(merge_gbs(torch, ulys, os_, lse, args.steps), 1)

@@ -183,8 +183,9 @@ int ulys_lse_merge(int n_parts, const void* const* o_parts, const float* const* 
  * accepted when G calls take no more rounds than the one call over all the
  * rank's heads, i.e. G * ceil(W / G / cus) <= ceil(W / cus) with
  * W = batch * (Hq/P) * ceil(rows_q / 256) * C, C the automatic key-range
- * split of the shape (ulys_attend_splits; it does not depend on the head
- * count, so it is the same for every G).  Returns the count (>= 1; 1 = keep
+ * split of the shape (ulys_attend_splits), or W = batch * (Hq/P) * R under
+ * an automatic range split R (ulys_attend_ranges); neither depends on the
+ * head count, so they are the same for every G.  Returns the count (>= 1; 1 = keep
  * the sequential single call); layout->groups is ignored.
  * Rules: the layout rules with groups = 1; compute_units >= 1 (ULYS_EINVAL).
  */
@@ -241,6 +242,15 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * 2 GiB, or one head's partials when those alone need more; a call needing
  * more runs its heads in several launches); calls on one stream share it in
  * stream order.
+ *
+ * Range split (automatic when C = 1, see ulys_attend_ranges): the (query
+ * tile, key tile) pairs of each (b, head), taken query tile by query tile,
+ * are cut into R near-equal runs, one workgroup each, so that a call's
+ * workgroups fill whole rounds of CUs with less than a query tile each.  A
+ * query tile inside one run is written directly; the pieces of a tile cut
+ * by run ends write fp32 partials (same workspace) that a second kernel
+ * combines in run order with the log-sum-exp weights.  R depends on (batch,
+ * rows, compute units) only, so the head-subset rule holds here too.
  */
 int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       const void* q, const void* k, const void* v, int qk_dtype,
@@ -269,10 +279,12 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  * so this cannot be rejected up front).  Query rows are never masked.
  * Rules: as ulys_attend_group with q_rows, kv_rows >= 1; key_mask 4-byte
  * aligned; with a key mask kv_rows <= 262144 (ULYS_EUNSUPPORTED otherwise).
- * key_splits: 0 = automatic (ulys_attend_splits of the device), 1 = no
- * split, 2..16 = that many key-range runs (outside [0, 16]: ULYS_EINVAL);
- * runs are near-equal shares of the processed key tiles, and a run without
- * tiles contributes nothing.
+ * key_splits: 0 = automatic (ulys_attend_splits, else ulys_attend_ranges,
+ * of the device), 1 = no split, 2..16 = that many key-range runs per query
+ * tile, -R = a range split into R runs per (b, head) (1 <= R <= 4096 and
+ * R <= 32 x the query tiles ceil(q_rows / 256)); anything else ULYS_EINVAL.
+ * Runs are near-equal shares of the processed key tiles (of the query-tile
+ * by key-tile pairs for -R), and a run without tiles contributes nothing.
  * ulys_attend_group(B, rows, ...) equals ulys_attend_group_ex(B, rows, rows,
  * ..., key_mask = NULL, key_splits = 0, ...), and a mask that marks exactly
  * the keys outside the gaps gives the same bytes as the gaps (at equal
@@ -304,6 +316,27 @@ int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, in
  * (ULYS_EINVAL) if an argument is < 1.
  */
 int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units);
+
+/*
+ * ulys_attend_ranges -- the automatic range split of an attention call.
+ *
+ * Source: as ulys_attend_splits (one launch per call whose workgroup count
+ * the shape fixes; partial attentions over disjoint key sets combined by
+ * their log-sum-exp).
+ *
+ * Returns the run count R > 0 that ulys_attend_group uses for (batch,
+ * q_rows, kv_rows) on compute_units CUs when ulys_attend_splits gives 1, else
+ * 0 (no range split).  Candidates are the multiples of compute_units / 8
+ * above the query tiles T = ceil(q_rows / 256) and up to 2T; the R minimising
+ * a model of the launch time averaged over calls of 2, 4, 8, 10 and 16 heads
+ * is taken if it beats no split by 3%.  The model: a round of a <= cus
+ * one-tile workgroups takes max(0.74, (a / cus)^0.35) of a full round (the
+ * device's throughput grows as the 0.65th power of its busy CUs); a run does
+ * T / R of a key sweep plus two pieces' start-up of six key tiles; the merge
+ * moves 18 bytes per output element.  Host-only: enqueues nothing.  A
+ * negative status (ULYS_EINVAL) if an argument is < 1.
+ */
+int ulys_attend_ranges(int batch, int q_rows, int kv_rows, int compute_units);
 
 /*
  * ulys_unpack -- inverse of ulys_pack for the output of (rank, group).

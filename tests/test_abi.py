@@ -141,9 +141,12 @@ def test_attend_ex_rules(U):
     assert _attend_ex(U, mask=FAKE + 2) == -1                          # mask words 4-byte aligned
     assert _attend_ex(U, nk=262144 + 64, mask=FAKE) == -2              # key-mask tile list limit
     assert "key mask" in U.last_error()
-    assert _attend_ex(U, splits=-1) == -1                              # key_splits in [0, 16]
+    assert _attend_ex(U, splits=-4097) == -1                           # key_splits in [-4096, 16]
     assert _attend_ex(U, splits=17) == -1
     assert "key_splits" in U.last_error()
+    assert _attend_ex(U, splits=-33) == -1                             # ranges: at most 32 per query tile
+    assert "per query tile" in U.last_error()
+    assert _attend_ex(U, nq=257, splits=-65) == -1                     # (2 query tiles: 64 ranges)
 
 
 def test_attend_splits_rule(U):
@@ -164,6 +167,26 @@ def test_attend_splits_rule(U):
         assert c == 1 or (args[2] + 63) // 64 >= 16 * c
     assert U.call_raw("ulys_attend_splits", 0, 1, 1, 1) == -1
     assert U.call_raw("ulys_attend_splits", 1, 1, 1, 0) == -1
+
+
+def test_attend_ranges_rule(U):
+    """The automatic range split (taken only where the key-range split is 1): host arithmetic only."""
+    # the Wan share: 107 query tiles per head -> 128 runs (0.84 tile each): a 2-head call is one full
+    # round of 256 workgroups, a 10-head call five (measured: +1 to +7% and +7% over no split)
+    assert U.ulys_attend_ranges(1, 27280, 27280, 256) == 128
+    assert U.ulys_attend_ranges(1, 1500, 6000, 256) == 0                 # the key-range split (5) applies
+    assert U.ulys_attend_ranges(1, 65536, 65536, 256) == 0               # 256 tiles per head fill the CUs
+    assert U.ulys_attend_ranges(1, 32760, 32760, 256) == 0               # 128 tiles: 2 heads fill the CUs
+    assert U.ulys_attend_ranges(1, 256, 1000, 256) == 0                  # one query tile: no candidate
+    for args in [(1, 27280, 27280, 256), (1, 24000, 24000, 256), (2, 20000, 30000, 304), (1, 9000, 70000, 80),
+                 (3, 27280, 27280, 256)]:
+        r = U.ulys_attend_ranges(*args)
+        qt = (args[1] + 255) // 256
+        cus = args[3]
+        assert r == 0 or (r % (cus // 8) == 0 and qt < r <= 2 * qt and r <= 4096)
+        assert r == 0 or U.ulys_attend_splits(*args) == 1
+    assert U.call_raw("ulys_attend_ranges", 0, 1, 1, 1) == -1
+    assert U.call_raw("ulys_attend_ranges", 1, 1, 1, 0) == -1
 
 
 def test_unpack_and_amax_rules(U):

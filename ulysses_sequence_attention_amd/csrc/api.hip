@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/ulys.h"
 #include "internal.h"
 
@@ -141,6 +143,62 @@ int auto_splits(long long batch, long long q_rows, long long kv_rows, int cus) {
   return best;
 }
 
+// Automatic range split of a call that auto_splits leaves unsplit: R equal
+// runs of each (b, head)'s (query tile, key tile) sequence, so that the
+// workgroups fill whole rounds of CUs with less than one query tile each.
+// Candidates: multiples of cus / 8 between the query tiles and twice them;
+// the R that minimises the modelled time averaged over 2, 4, 8, 10 and 16
+// heads (independent of the head count, as for C), kept only if it beats no
+// split by 3%; 0 = none.  Model (fitted to MI355X launches of 128, 214 and
+// 256 one-tile workgroups at the 27280-key shape, and to 10-head calls):
+//  * a round of a workgroups (a <= cus, one per CU) takes
+//    max(0.74, (a / cus)^0.35) of a full round: the device's throughput grows
+//    only as the 0.65th power of the busy CUs, with a floor for small rounds;
+//  * a range does qtiles / R of a key sweep plus two pieces' start-up (six
+//    key tiles each);
+//  * the merge moves 18 bytes per output element (two fp32 pieces written
+//    and read, one bf16 write), priced as for the key-range split.
+int auto_ranges(long long batch, long long q_rows, long long kv_rows, int cus) {
+  const long long qt = (q_rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup;
+  const double nt = (double)((kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile);
+  const double kFloor = 0.74, kExp = 0.35, kStartTiles = 6.0, kGain = 0.97;
+  auto rounds = [&](double wgs, double per) {
+    const double full = floor(wgs / cus), rest = wgs - full * cus;
+    return per * (full + (rest > 0 ? fmax(kFloor, pow(rest / cus, kExp)) : 0.0));
+  };
+  static const int kHeads[] = {2, 4, 8, 10, 16};
+  constexpr int kNH = sizeof kHeads / sizeof kHeads[0];
+  const long long step = cus >= 8 ? cus / 8 : 1;
+  const long long rmax = std::min<long long>(std::min<long long>(2 * qt, ulys::kMaxRanges),
+                                             (long long)ulys::kMaxRangesPerTile * qt);
+  int best = 0;
+  double best_rel = kGain;
+  for (long long r = (qt / step + 1) * step; r <= rmax; r += step) {
+    double rel = 0.0;
+    for (int hq : kHeads) {
+      const double plain = rounds((double)batch * qt * hq, 1.0);
+      const double per = (double)qt / (double)r + 2.0 * kStartTiles / nt;
+      const double merge = hq * (double)batch * qt * 18.0 / (320.0 * nt);
+      rel += (rounds((double)batch * r * hq, per) + merge) / plain;
+    }
+    rel /= kNH;
+    if (rel < best_rel) {
+      best = (int)r;
+      best_rel = rel;
+    }
+  }
+  return best;
+}
+
+// The automatic key_splits value: C > 1 (key-range split), -R (range split)
+// or 1 (none).
+int auto_key_splits(long long batch, long long q_rows, long long kv_rows, int cus) {
+  const int c = auto_splits(batch, q_rows, kv_rows, cus);
+  if (c > 1) return c;
+  const int r = auto_ranges(batch, q_rows, kv_rows, cus);
+  return r > 0 ? -r : 1;
+}
+
 // Compute units of the current device (cached per device).
 int device_cus(int* cus) {
   static int cache[64];
@@ -227,8 +285,14 @@ int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head
   if (fp8 && ((uintptr_t)qk_amax & 3u)) return fail(ULYS_EINVAL, "qk_amax is not 4-byte aligned");
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(ULYS_EINVAL, "softmax_scale must be finite");
-  if (key_splits < 0 || key_splits > ulys::kMaxKeySplits)
-    return fail(ULYS_EINVAL, "key_splits %d outside [0, %d]", key_splits, ulys::kMaxKeySplits);
+  if (key_splits < -ulys::kMaxRanges || key_splits > ulys::kMaxKeySplits)
+    return fail(ULYS_EINVAL, "key_splits %d outside [%d, %d]", key_splits, -ulys::kMaxRanges, ulys::kMaxKeySplits);
+  if (key_splits < 0) {
+    const long long qtiles = ((long long)q_rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup;
+    if (-(long long)key_splits > qtiles * ulys::kMaxRangesPerTile)
+      return fail(ULYS_EINVAL, "%d ranges exceed %d per query tile (%lld tiles)", -key_splits,
+                  ulys::kMaxRangesPerTile, qtiles);
+  }
   if (key_mask != nullptr) {
     if ((uintptr_t)key_mask & 3u) return fail(ULYS_EINVAL, "key_mask is not 4-byte aligned");
     const long long tiles = ((long long)kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile;
@@ -271,11 +335,20 @@ int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head
 // The automatic key-range split (from the device's compute units and the
 // shape) of validated arguments; the first HIP call of an attention call.
 int resolve_splits(ulys::AttnArgs& a) {
+  if (a.splits < 0) {   // a range split: -splits ranges per (b, head)
+    a.ranges = -a.splits;
+    a.splits = 1;
+    return ULYS_OK;
+  }
   if (a.splits != 0) return ULYS_OK;
   int cus = 0;
   const int st = device_cus(&cus);
   if (st) return st;
-  a.splits = auto_splits(a.batch, a.q_rows, a.kv_rows, cus);
+  a.splits = auto_key_splits(a.batch, a.q_rows, a.kv_rows, cus);
+  if (a.splits < 0) {
+    a.ranges = -a.splits;
+    a.splits = 1;
+  }
   return ULYS_OK;
 }
 
@@ -493,6 +566,14 @@ int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units) {
   return auto_splits(batch, q_rows, kv_rows, compute_units);
 }
 
+int ulys_attend_ranges(int batch, int q_rows, int kv_rows, int compute_units) {
+  if (batch < 1 || q_rows < 1 || kv_rows < 1 || compute_units < 1)
+    return fail(ULYS_EINVAL, "batch, q_rows, kv_rows and compute_units must be >= 1");
+  ok();
+  return auto_splits(batch, q_rows, kv_rows, compute_units) > 1 ? 0
+                                                               : auto_ranges(batch, q_rows, kv_rows, compute_units);
+}
+
 int ulys_auto_groups(const ulys_layout* L, int compute_units) {
   if (compute_units < 1) return fail(ULYS_EINVAL, "compute_units must be >= 1");
   if (L == nullptr) return fail(ULYS_EINVAL, "layout is NULL");
@@ -508,9 +589,10 @@ int ulys_auto_groups(const ulys_layout* L, int compute_units) {
   // Workgroups of the one-call attention (256 query rows each, times the
   // automatic key-range split, which is the same for every group count; one
   // per CU at a time) and the rounds of CUs they take.
-  const long long splits = auto_splits(L->batch, rows, rows_kv, compute_units);
-  const long long wgs = (long long)L->batch * hq_rank * splits *
-                        ((rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup);
+  const long long ks = auto_key_splits(L->batch, rows, rows_kv, compute_units);
+  const long long per_head = ks < 0 ? -ks : ks * ((rows + ulys::kAttnRowsPerWorkgroup - 1) /
+                                                  ulys::kAttnRowsPerWorkgroup);
+  const long long wgs = (long long)L->batch * hq_rank * per_head;
   const long long rounds_one = (wgs + compute_units - 1) / compute_units;
   static const int kCandidates[] = {7, 5, 4, 3, 2};
   for (int G : kCandidates) {

@@ -156,8 +156,12 @@ void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int split = blockIdx.x / a.qtiles;   // key-range chunk of this workgroup
-  const int qtile = blockIdx.x - split * a.qtiles;
+  // This workgroup's work: with a range split (a.ranges > 0), range blockIdx.x
+  // of its (b, head)'s (query tile, key tile) sequence; otherwise query tile
+  // qtile0, key-range chunk `split` of a.splits.
+  const bool ranged = a.ranges > 0;
+  const int split = ranged ? 0 : blockIdx.x / a.qtiles;
+  const int qtile0 = ranged ? 0 : blockIdx.x - split * a.qtiles;
   const int hl = blockIdx.y;                  // head within this launch
   const int head = a.head0 + hl;
   const int b = blockIdx.z;
@@ -184,11 +188,20 @@ void attn_fwd_kernel(AttnArgs a) {
   // ---- Q fragments in registers (B operand of S^T = K Q^T) ----
   const size_t q_row_stride = (size_t)a.hq * D;            // elements
   const size_t kv_row_stride = (size_t)a.hkv * D;
-  const int qrow0 = qtile * kBM + wave * 32;
   constexpr int kQRegs = FP8 ? 8 : 4;                       // dwords per fragment
   unsigned int qf[C::kQKSteps][kQRegs];
-  {
-    const int row = qrow0 + l32;
+  // The thread index as a value the compiler cannot see through: per-lane
+  // addresses of the per-piece work (Q loads, output writes, merge) are
+  // formed from it inside the piece loop instead of being hoisted out of it
+  // and held in registers across the key loop.
+  auto fresh_tid = [&]() {
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(tid));
+    return t;
+  };
+  auto load_q = [&](int qrow0) {
+    const int ft = fresh_tid();
+    const int row = qrow0 + (ft & 31), hh = (ft >> 5) & 1;
     const unsigned char* qp = (const unsigned char*)a.q +
         (((size_t)b * qrows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
 #pragma unroll
@@ -202,7 +215,7 @@ void attn_fwd_kernel(AttnArgs a) {
         qf[kk][part * 4 + 2] = x.z; qf[kk][part * 4 + 3] = x.w;
       }
     }
-  }
+  };
 
   // ---- global -> LDS staging of one K/V tile (direct 16-byte loads) ----
   // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i, so each
@@ -272,19 +285,26 @@ void attn_fwd_kernel(AttnArgs a) {
   };
 
   // ---- running state ----
+  // (set by reset_state at the start of every piece of work)
   f32x16 o[C::kDB];
-#pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m_run = -INFINITY;   // running max of c*log2e*s (lazy)
-  float negm = 0.0f;         // -m_run, or 0 while m_run is -inf
+  float m_run;   // running max of c*log2e*s (lazy)
+  float negm;    // -m_run, or 0 while m_run is -inf
   // A block raises m_run when this lane's sum of its 16 probabilities exceeds
   // thr: 2^8 (probabilities are >= 0, so a sum <= 2^8 bounds each of them by
   // 2^8, and a probability above 2^8 makes the sum exceed it), or -1 while
   // m_run is -inf (every block raises until the row has a finite max).
-  float thr = -1.0f;
-  float l_run = 0.0f;        // row sum (this lane's half of the keys)
+  float thr;
+  float l_run;   // row sum (this lane's half of the keys)
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    m_run = -INFINITY;
+    negm = 0.0f;
+    thr = -1.0f;
+    l_run = 0.0f;
+  };
 
   // Barrier publishing the next tile: this wave's loads of that tile have
   // landed (s_waitcnt vmcnt(N): at most the later tiles' loads still in flight;
@@ -310,16 +330,18 @@ void attn_fwd_kernel(AttnArgs a) {
   //  compile-time offset; other stages are reached by a scalar delta.
   constexpr int kKOffs = FP8 ? 2 * C::kQKSteps : C::kQKSteps;
   int kcur[kKOffs];
+  auto reset_kcur = [&]() {
 #pragma unroll
-  for (int kk = 0; kk < C::kQKSteps; ++kk) {
-    const int sw = l32 & (C::kKSwz - 1);
-    if constexpr (!FP8) {
-      kcur[kk] = C::kKTile + l32 * C::kKRow + (((kk * 2 + hh) ^ sw) * 16);
-    } else {
-      kcur[2 * kk] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2) ^ sw) * 16);
-      kcur[2 * kk + 1] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2 + 1) ^ sw) * 16);
+    for (int kk = 0; kk < C::kQKSteps; ++kk) {
+      const int sw = l32 & (C::kKSwz - 1);
+      if constexpr (!FP8) {
+        kcur[kk] = C::kKTile + l32 * C::kKRow + (((kk * 2 + hh) ^ sw) * 16);
+      } else {
+        kcur[2 * kk] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2) ^ sw) * 16);
+        kcur[2 * kk + 1] = C::kKTile + l32 * C::kKRow + (((kk * 4 + hh * 2 + 1) ^ sw) * 16);
+      }
     }
-  }
+  };
   //  V (A operand of O^T, transposing reads): within 16 lanes, lane 4j+t reads
   //  row key0 + j at head-dim d0 + 4t.. (see read_v).
   const int g16 = lane >> 4, jrow = (lane >> 2) & 3, tcol = lane & 3;
@@ -520,10 +542,6 @@ void attn_fwd_kernel(AttnArgs a) {
   f32x16 sA, sB;
   VFrag vf;
   bf16x8 pA[2], pB[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pA[e][i] = (__bf16)0.0f;
 
   constexpr int kPVMfma = 2 * C::kDB;
   constexpr int kQKMfma = C::kQKSteps;
@@ -611,128 +629,213 @@ void attn_fwd_kernel(AttnArgs a) {
         tile_list[pos++] = (unsigned short)t;
     __syncthreads();
   }
-  // This workgroup's chunk of the sequence: positions [p0, p0 + n), the
-  // split-th of `splits` near-equal runs (a function of the tile sequence
-  // alone, the same for every head).
-  const int p0 = (int)(((long long)split * nseq) / a.splits);
-  const int n = (int)(((long long)(split + 1) * nseq) / a.splits) - p0;
-  // (uniform across the workgroup: kept in scalar registers)
-  auto seq_tile = [&](int pos) {
-    pos += p0;
-    if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
-    else return pos < skip_first ? pos : pos + nskip;
-  };
-  // Position pos goes to stage pos % kStages; past the end the last tile is
-  // loaded again, which keeps every wave's load count per tile uniform.
-  auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, n - 1)), st); };
-
-  if (n > 0) {   // else (an empty chunk, or a mask that left no valid key) o = 0, lse = -inf
-    load_pos(0, std::integral_constant<int, 0>{});
-    load_pos(1, std::integral_constant<int, 1>{});
-    if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    {
-      KFrag kf;
-      read_k(-C::kKTile, B0{}, kf);
-      sA = qk(kf);
-      read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
+  // Pieces of work: (query tile qtile, positions [p0, p0 + n) of the tile
+  // sequence).  A key-range chunk is one piece: the split-th of `splits`
+  // near-equal runs (a function of the tile sequence alone, the same for
+  // every head).  A range of the sequence of units u = qtile * nunits + pos
+  // is a run of pieces: the end of one tile, whole tiles, the start of
+  // another.  (A mask that leaves no valid key gives each tile one empty
+  // unit, so that its zero output is written.)
+  // A range that starts inside a tile and runs past its end takes that
+  // tile's tail last: every other piece starts at the first key tile, so the
+  // workgroups of a launch keep walking the keys nearly in step (two key
+  // positions, a fixed distance apart, at any time) and share K/V tiles in L2.
+  const int nunits = max(nseq, 1);
+  const long long units = (long long)a.qtiles * nunits;
+  long long u = 0, uend = 1, ustart = 0, tail_u = -1, tail_end = -1;
+  if (ranged) {
+    ustart = u = (long long)blockIdx.x * units / a.ranges;
+    uend = (long long)(blockIdx.x + 1) * units / a.ranges;
+    const long long next_tile = (ustart / nunits + 1) * nunits;
+    if (ustart % nunits != 0 && next_tile < uend) {
+      tail_u = ustart;
+      tail_end = next_tile;
+      u = next_tile;
     }
-    int tc = seq_tile(0);
-    // Tiles with keys outside [0, rows) or inside the gap: the one holding the
-    // gap's first key, the one holding its last, and the ragged last tile
-    // (ascending; tiles are visited in ascending order, so one compare per
-    // tile against the next of them decides whether its blocks take the
-    // per-block range test).
-    constexpr int kNone = 0x7fffffff;
-    const int dz = tail_tile >= 0 ? tail_tile : kNone;
-    const int dx = gs < ge ? gs / kBN : dz, dy = gs < ge ? (ge - 1) / kBN : dz;
-    auto next_dirty = [&](int t) { return dx > t ? dx : dy > t ? dy : dz > t ? dz : kNone; };
-    int nd = next_dirty(tc - 1);
-    bool dc = tc == nd;
-    if (dc) nd = next_dirty(tc);
-    // mask words of the tile's second block (mw1) and of the next tile's blocks
-    // (fetched a block ahead: each is a scalar value once it is used)
-    unsigned mw1 = mask_word(tc * kBN + 32);
-    iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
-              tc * kBN,
-              __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), dc, sA, sB, pA, pB);
-    tile_barrier();
-
-    // Position i (stage SA): its second block, then the first block of
-    // position i+1 (stage SB).  Position i + kStages - 1 is loaded first, into
-    // SP, the stage of position i-1, which every wave has finished with.  The
-    // next tile's key-mask words are fetched a block ahead.  Each step ends
-    // with a barrier.  Returns false after the last position.
-    auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
-      load_pos(i + kStages - 1, SP);
-      const int tn = i + 1 < n ? seq_tile(i + 1) : tc;
-      const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
-      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
-                tc * kBN + 32,
-                __builtin_amdgcn_readfirstlane(mw1), dc, sB, sA, pB, pA);
-      if (i + 1 >= n) return false;
-      tc = tn;
-      mw1 = wn1;
-      dc = tc == nd;
-      if (dc) nd = next_dirty(tc);
-      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
-                __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
-      // the next step reads K from the stage after SB
-      const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
-#pragma unroll
-      for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
-      tile_barrier();
-      return true;
-    };
-    int sa = 0;
-    for (int i = 0;; ++i) {
-      const int sb = sa == kStages - 1 ? 0 : sa + 1;
-      if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
-      sa = sb;
-    }
-    pv(vf, pA);
   }
+  if (ranged && blockIdx.x == 0 && hl == 0 && tid == 0) a.range_nseq[b] = nseq;
+  reset_kcur();
+  for (;;) {
+    if (u >= uend) {
+      if (tail_u < 0) break;
+      u = tail_u;
+      uend = tail_end;
+      tail_u = -1;
+    }
+    int qtile, p0, n;
+    if (ranged) {
+      qtile = (int)(u / nunits);
+      p0 = (int)(u - (long long)qtile * nunits);
+      n = (int)min(uend - u, (long long)(nunits - p0));
+      if (nseq == 0) n = 0;
+    } else {
+      qtile = qtile0;
+      p0 = (int)(((long long)split * nseq) / a.splits);
+      n = (int)(((long long)(split + 1) * nseq) / a.splits) - p0;
+    }
+    const long long upiece = (long long)qtile * nunits + p0;
+    u = ranged ? upiece + max(n, 1) : uend;
+    const int qrow0 = qtile * kBM + wave * 32;
+    load_q(qrow0);
+    reset_state();
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pA[e][i] = (__bf16)0.0f;
 
-  // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
-  // (with a key-range split: o in fp32 and lse in the log2 domain, per split)
-  {
-    const int row = qrow0 + l32;
+    // (uniform across the workgroup: kept in scalar registers)
+    auto seq_tile = [&](int pos) {
+      pos += p0;
+      if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
+      else return pos < skip_first ? pos : pos + nskip;
+    };
+    // Position pos goes to stage pos % kStages; past the end the last tile is
+    // loaded again, which keeps every wave's load count per tile uniform.
+    auto load_pos = [&](int pos, auto st) { load_tile(seq_tile(min(pos, n - 1)), st); };
+
+    if (n > 0) {   // else (an empty chunk, or a mask that left no valid key) o = 0, lse = -inf
+      load_pos(0, std::integral_constant<int, 0>{});
+      load_pos(1, std::integral_constant<int, 1>{});
+      if constexpr (kStages > 3) load_pos(2, std::integral_constant<int, 2>{});
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      {
+        KFrag kf;
+        read_k(-C::kKTile, B0{}, kf);
+        sA = qk(kf);
+        read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
+      }
+      int tc = seq_tile(0);
+      // Tiles with keys outside [0, rows) or inside the gap: the one holding the
+      // gap's first key, the one holding its last, and the ragged last tile
+      // (ascending; tiles are visited in ascending order, so one compare per
+      // tile against the next of them decides whether its blocks take the
+      // per-block range test).
+      constexpr int kNone = 0x7fffffff;
+      const int dz = tail_tile >= 0 ? tail_tile : kNone;
+      const int dx = gs < ge ? gs / kBN : dz, dy = gs < ge ? (ge - 1) / kBN : dz;
+      auto next_dirty = [&](int t) { return dx > t ? dx : dy > t ? dy : dz > t ? dz : kNone; };
+      int nd = next_dirty(tc - 1);
+      bool dc = tc == nd;
+      if (dc) nd = next_dirty(tc);
+      // mask words of the tile's second block (mw1) and of the next tile's blocks
+      // (fetched a block ahead: each is a scalar value once it is used)
+      unsigned mw1 = mask_word(tc * kBN + 32);
+      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
+                tc * kBN,
+                __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), dc, sA, sB, pA, pB);
+      tile_barrier();
+
+      // Position i (stage SA): its second block, then the first block of
+      // position i+1 (stage SB).  Position i + kStages - 1 is loaded first, into
+      // SP, the stage of position i-1, which every wave has finished with.  The
+      // next tile's key-mask words are fetched a block ahead.  Each step ends
+      // with a barrier.  Returns false after the last position.
+      auto step = [&](int i, auto SA, auto SB, auto SP) ULYS_INLINE {
+        load_pos(i + kStages - 1, SP);
+        const int tn = i + 1 < n ? seq_tile(i + 1) : tc;
+        const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
+        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
+                  tc * kBN + 32,
+                  __builtin_amdgcn_readfirstlane(mw1), dc, sB, sA, pB, pA);
+        if (i + 1 >= n) return false;
+        tc = tn;
+        mw1 = wn1;
+        dc = tc == nd;
+        if (dc) nd = next_dirty(tc);
+        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
+                  __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
+        // the next step reads K from the stage after SB
+        const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
+  #pragma unroll
+        for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
+        tile_barrier();
+        return true;
+      };
+      int sa = 0;
+      for (int i = 0;; ++i) {
+        const int sb = sa == kStages - 1 ? 0 : sa + 1;
+        if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
+        sa = sb;
+      }
+      pv(vf, pA);
+      // back to the first step's K offsets (the last step, at stage sa, read
+      // K from stage sa + 1 and did not move them)
+      const int kback = ((sa == kStages - 1 ? 0 : sa + 1) - 1) * C::kKTile;
+#pragma unroll
+      for (int k = 0; k < kKOffs; ++k) kcur[k] -= kback;
+    }
+
+    // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
+    // (a key-range chunk, or a range's piece of a tile it shares with other
+    // ranges: o in fp32 and lse in the log2 domain, to be merged)
+    const int ft = fresh_tid();
+    const int row = qrow0 + (ft & 31), hh = (ft >> 5) & 1, l32 = ft & 31;
     const float l = lane_swap_sum(l_run);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (row < qrows && a.splits > 1) {
-      const size_t prow = ((size_t)split * a.batch + b) * qrows + row;
-      float* pp = a.part_o + (prow * a.hsub + hl) * D;
+    const bool whole = !ranged || (p0 == 0 && n == nseq);
+    if (!ranged && a.splits > 1) {
+      if (row < qrows) {
+        const size_t prow = ((size_t)split * a.batch + b) * qrows + row;
+        float* pp = a.part_o + (prow * a.hsub + hl) * D;
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
+        for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                            o[db][4 * r4 + 3] * inv};
-          *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
-        }
-      if (hh == 0)
-        a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] =
-            l > 0.0f ? m_run + __log2f(l) : -INFINITY;
-    } else if (row < qrows) {
-      uint16_t* op = a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                              o[db][4 * r4 + 3] * inv};
+            *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
+          }
+        if (hh == 0)
+          a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] =
+              l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+      }
+    } else if (whole) {
+      if (row < qrows) {
+        uint16_t* op = a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D;
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
+        for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x2 lo = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv};
-          const f32x2 hi = {o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
-          const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
-          const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
-          u32x2 w;
-          w.x = __builtin_bit_cast(unsigned int, blo);
-          w.y = __builtin_bit_cast(unsigned int, bhi);
-          *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
-        }
-      if (a.lse != nullptr && hh == 0)
-        a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x2 lo = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv};
+            const f32x2 hi = {o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
+            const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
+            const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
+            u32x2 w;
+            w.x = __builtin_bit_cast(unsigned int, blo);
+            w.y = __builtin_bit_cast(unsigned int, bhi);
+            *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
+          }
+        if (a.lse != nullptr && hh == 0)
+          a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+      }
+    } else {
+      // A piece of a tile shared with neighbouring ranges (merged by
+      // range_merge_kernel): slot 0 if it is this range's first piece, 1 if
+      // its last.
+      const int slot = upiece == ustart ? 0 : 1;
+      const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + blockIdx.x) * 2 + slot;
+      if (row < qrows) {
+        float* pp = a.part_o + (pidx * kBM + wave * 32 + l32) * D;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                              o[db][4 * r4 + 3] * inv};
+            *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
+          }
+        if (hh == 0) a.part_lse[pidx * kBM + wave * 32 + l32] = l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+      }
+    }
+    if (u < uend || tail_u >= 0) {
+      // the next piece refills the ring: every tile load of this one has
+      // landed and every wave is done reading it
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      asm volatile("" ::: "memory");
+      __syncthreads();
     }
   }
 }
@@ -801,15 +904,96 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(AttnArgs a) 
     a.lse[((size_t)b * a.hq + head) * a.q_rows + row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
+// Merge of a range split's cut tiles.  Workgroup: one (query tile, head, b).
+// The tile's pieces come from the non-empty ranges between the one holding
+// its first unit and the one holding its last (range of unit x: the largest
+// r with r U / R <= x); a tile within one range was written by the attention
+// kernel and is skipped.  Combination in range order, as for key-range
+// chunks: M = max lse_r, w_r = 2^(lse_r - M), o = sum_r w_r o_r / sum_r w_r,
+// lse = (M + log2 sum_r w_r) ln 2.  Thread: 4 head dims of kRowsPerPass rows
+// (consecutive lanes read consecutive 16-byte chunks of a row), all of a
+// piece's loads issued before they are used.
+template <int D>
+__global__ __launch_bounds__(kThreads) void range_merge_kernel(AttnArgs a) {
+  constexpr int kC4 = D / 4;                     // 16-byte chunks per row
+  constexpr int kRowsPerPass = kThreads / kC4;   // rows the workgroup covers at once
+  constexpr int kPasses = kBM / kRowsPerPass;
+  const int qtile = blockIdx.x, hl = blockIdx.y, b = blockIdx.z;
+  const long long nunits = max(a.range_nseq[b], 1);
+  const long long units = (long long)a.qtiles * nunits, R = a.ranges;
+  auto range_start = [&](long long r) { return r * units / R; };
+  auto range_of = [&](long long x) { return (int)(((x + 1) * R - 1) / units); };
+  const long long t0 = (long long)qtile * nunits;
+  const int rf = range_of(t0), rl = range_of(t0 + nunits - 1);
+  if (rf == rl) return;   // (a range holds the whole tile)
+  const int c4 = threadIdx.x % kC4, r0 = threadIdx.x / kC4;
+  const size_t pbase = ((size_t)b * a.hsub + hl) * (size_t)R;
+  auto piece = [&](int r) { return ((pbase + r) * 2 + (range_start(r) < t0 ? 1 : 0)) * kBM; };
+  auto nonempty = [&](int r) { return range_start(r + 1) > range_start(r); };
+  float mx[kPasses], wsum[kPasses];
+  f32x4 acc[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    mx[p] = -INFINITY;
+    wsum[p] = 0.0f;
+    acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int r = rf; r <= rl; ++r)
+    if (nonempty(r)) {
+      const size_t pi = piece(r);
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) mx[p] = fmaxf(mx[p], a.part_lse[pi + p * kRowsPerPass + r0]);
+    }
+  for (int r = rf; r <= rl; ++r)
+    if (nonempty(r)) {
+      const size_t pi = piece(r);
+      float lv[kPasses];
+      f32x4 x[kPasses];
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const size_t row = pi + p * kRowsPerPass + r0;
+        lv[p] = a.part_lse[row];
+        x[p] = __builtin_nontemporal_load((const f32x4*)(a.part_o + row * D) + c4);
+      }
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p)
+        if (mx[p] != -INFINITY) {
+          const float w = __builtin_amdgcn_exp2f(lv[p] - mx[p]);   // 0 for a piece with no key
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[p][j] += w * x[p][j];
+          wsum[p] += w;
+        }
+    }
+  const int head = a.head0 + hl;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int row = qtile * kBM + p * kRowsPerPass + r0;
+    if (row >= a.q_rows) continue;
+    const float inv = wsum[p] > 0.0f ? 1.0f / wsum[p] : 0.0f;
+    const f32x2 lo = {acc[p][0] * inv, acc[p][1] * inv}, hi = {acc[p][2] * inv, acc[p][3] * inv};
+    u32x2 out;
+    out.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(lo, bf16x2));
+    out.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(hi, bf16x2));
+    *(u32x2*)(a.o + (((size_t)b * a.q_rows + row) * a.hq + head) * D + 4 * c4) = out;
+    if (a.lse != nullptr && c4 == 0)
+      a.lse[((size_t)b * a.hq + head) * a.q_rows + row] = wsum[p] > 0.0f ? (mx[p] + __log2f(wsum[p])) * kLn2 : -INFINITY;
+  }
+}
+
 template <int D, bool FP8>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.qtiles * a.splits, a.hsub, a.batch);
+  dim3 grid(a.ranges > 0 ? a.ranges : a.qtiles * a.splits, a.hsub, a.batch);
   if (a.key_mask != nullptr)
     hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, true>), grid, dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, false>), grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (a.ranges > 0) {
+    hipLaunchKernelGGL((range_merge_kernel<D>), dim3(a.qtiles, a.hsub, a.batch), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.splits == 1) return hipSuccess;
   const size_t threads = (size_t)a.batch * a.q_rows * a.hsub * (D / 8);
   hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)((threads + kMergeThreads - 1) / kMergeThreads)),
                      dim3(kMergeThreads), 0, s, a);
@@ -860,19 +1044,28 @@ hipError_t launch(const AttnArgs& in, hipStream_t s) {
   a.qtiles = (a.q_rows + kBM - 1) / kBM;
   a.head0 = 0;
   a.hsub = a.hq;
-  if (a.splits <= 1) {
+  if (a.ranges > 0) a.splits = 1;
+  if (a.splits <= 1 && a.ranges == 0) {
     a.splits = 1;
     return launch_one<D, FP8>(a, s);
   }
-  const size_t o_per_head = (size_t)a.splits * a.batch * a.q_rows * D * sizeof(float);
-  const size_t l_per_head = (size_t)a.splits * a.batch * a.q_rows * sizeof(float);
+  size_t o_per_head, l_per_head;
+  if (a.ranges > 0) {
+    o_per_head = (size_t)a.batch * a.ranges * 2 * kBM * D * sizeof(float);
+    l_per_head = (size_t)a.batch * a.ranges * 2 * kBM * sizeof(float);
+  } else {
+    o_per_head = (size_t)a.splits * a.batch * a.q_rows * D * sizeof(float);
+    l_per_head = (size_t)a.splits * a.batch * a.q_rows * sizeof(float);
+  }
   const size_t per_head = o_per_head + l_per_head;
   const int hsub = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.hq, kSplitWorkspaceCap / per_head));
+  const size_t nseq_bytes = (size_t)a.batch * sizeof(int);
   void* ws = nullptr;
-  hipError_t e = split_workspace(s, per_head * hsub, &ws);
+  hipError_t e = split_workspace(s, per_head * hsub + nseq_bytes, &ws);
   if (e != hipSuccess) return e;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + o_per_head * hsub);
+  a.range_nseq = (int*)((char*)a.part_lse + l_per_head * hsub);
   for (int h0 = 0; h0 < a.hq; h0 += hsub) {
     a.head0 = h0;
     a.hsub = std::min(hsub, a.hq - h0);

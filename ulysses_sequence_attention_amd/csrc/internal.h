@@ -15,6 +15,8 @@ constexpr int kAttnRowsPerWorkgroup = 256;   // query rows per attention workgro
 constexpr int kAttnKeysPerTile = 64;         // keys per attention LDS tile
 constexpr int kMaxMaskTiles = 4096;          // key tiles (262144 keys) an attention call with a key mask may span
 constexpr int kMaxKeySplits = 16;            // key-range chunks per query tile
+constexpr int kMaxRanges = 4096;             // ranges per (batch, head) of a range split
+constexpr int kMaxRangesPerTile = 32;        // ... and per query tile
 constexpr int kMaxAmaxTensors = 64;
 
 // Geometry of one pack/unpack launch, resolved on the host.
@@ -79,6 +81,17 @@ struct AttnArgs {
   int splits, qtiles, head0, hsub;
   float* part_o;
   float* part_lse;
+  // Range split (ranges = R > 0; splits is then 1): workgroup r of a
+  // (b, head) takes units [r U / R, (r + 1) U / R) of the sequence
+  // u = query tile * key tiles + key-tile position (U units), i.e. the end of
+  // one query tile, whole tiles, the start of another.  A tile within one
+  // range is written directly; the pieces of a tile cut by range ends leave
+  // fp32 results in part_o [batch][hsub][R][2][kBM][D] / part_lse
+  // [batch][hsub][R][2][kBM] (slot 0: the range's first piece, 1: its last)
+  // for a merge kernel that combines them in range order.  range_nseq[b]:
+  // key tiles with a valid key of batch b (written by the attention kernel).
+  int ranges;
+  int* range_nseq;
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

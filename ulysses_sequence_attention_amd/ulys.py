@@ -49,6 +49,8 @@ _lib.ulys_attend_group_ex.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i,
 _lib.ulys_attend_group_ex.restype = _i
 _lib.ulys_attend_splits.argtypes = [_i, _i, _i, _i]
 _lib.ulys_attend_splits.restype = _i
+_lib.ulys_attend_ranges.argtypes = [_i, _i, _i, _i]
+_lib.ulys_attend_ranges.restype = _i
 _lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.POINTER(_vp), _vp]
 _lib.ulys_unpack.restype = _i
 _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -65,6 +67,7 @@ _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits",
+            "ulys_attend_ranges",
             "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror",
             "ulys_last_error")
 
@@ -228,7 +231,8 @@ def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
 
     ``key_mask``: device int32/uint32 words ``[B, ceil(Nk/32)]``, bit ``j % 32`` of word ``j // 32`` set for a
     valid key ``j``, or None (all keys valid).  ``key_gaps`` as for :func:`ulys_attend_group`.
-    ``key_splits``: 0 = automatic (:func:`ulys_attend_splits`), 1 = none, 2..16 = that many key-range runs.
+    ``key_splits``: 0 = automatic (:func:`ulys_attend_splits`, else :func:`ulys_attend_ranges`), 1 = none,
+    2..16 = that many key-range runs per query tile, ``-R`` = a range split into R runs per (b, head).
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
@@ -325,6 +329,13 @@ def ulys_lse_merge(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tenso
 def ulys_attend_splits(batch: int, q_rows: int, kv_rows: int, compute_units: int = 256) -> int:
     """The automatic key-range split (run count) of an attention call of this shape on ``compute_units`` CUs."""
     st = _lib.ulys_attend_splits(int(batch), int(q_rows), int(kv_rows), int(compute_units))
+    _check(min(st, 0))
+    return st
+
+
+def ulys_attend_ranges(batch: int, q_rows: int, kv_rows: int, compute_units: int = 256) -> int:
+    """The automatic range split (runs per (b, head), 0 = none) of an attention call of this shape."""
+    st = _lib.ulys_attend_ranges(int(batch), int(q_rows), int(kv_rows), int(compute_units))
     _check(min(st, 0))
     return st
 
