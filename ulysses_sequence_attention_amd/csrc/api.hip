@@ -2,8 +2,10 @@
 //
 // Every rule is checked before anything touches the HIP runtime, so a bad
 // call returns its status with nothing enqueued (and can be exercised on a
-// machine without a GPU).  The library allocates nothing and keeps no state
-// except the per-thread text of the last validation failure.
+// machine without a GPU).  This file allocates nothing and keeps no state
+// except the per-thread text of the last validation failure and the cached
+// compute-unit count per device (the split attention's workspace belongs to
+// the attention launcher).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
