@@ -243,7 +243,7 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * more runs its heads in several launches); calls on one stream share it in
  * stream order.
  *
- * Range split (automatic when C = 1, see ulys_attend_ranges): the (query
+ * Range split (automatic, see ulys_attend_ranges): the (query
  * tile, key tile) pairs of each (b, head), taken query tile by query tile,
  * are cut into R near-equal runs, one workgroup each, so that a call's
  * workgroups fill whole rounds of CUs with less than a query tile each.  A
@@ -306,14 +306,17 @@ int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, in
  * (flashdreams cp.py, ContextParallelAttention._impl_ring).
  *
  * Returns the run count C >= 1 that ulys_attend_group uses for
- * (batch, q_rows, kv_rows) on a device with compute_units CUs: the C in
- * [1, 16] (each run >= 16 key tiles) minimising a model of the launch time
- * averaged over calls of 2, 4, 8 and 16 heads, if it beats C = 1 by 3%.
- * The model: workgroups run in rounds of one per CU, with the device's
- * throughput saturating at 84% of its CUs busy; a run costs 1/C of the keys
- * plus about six key tiles of start-up; the merge moves 4C + 2 bytes per
- * output element.  Host-only: enqueues nothing.  A negative status
- * (ULYS_EINVAL) if an argument is < 1.
+ * (batch, q_rows, kv_rows) on a device with compute_units CUs (1: no
+ * key-range split).  One model chooses among no split, C in [2, 16] (each
+ * run >= 16 key tiles) and the range split of ulys_attend_ranges: the choice
+ * minimising the modelled launch time averaged over calls of 2, 4, 8, 10 and
+ * 16 heads, if it beats no split by 3%.  The model: workgroups run in rounds
+ * of one per CU and a round of a workgroups takes max(0.8, (a / cus)^0.25)
+ * of a full one (the device's throughput grows as the 0.75th power of its
+ * busy CUs); a workgroup does its share of the keys plus eight key tiles of
+ * start-up per piece; the merge moves 4C + 2 (or, for a range split, 18)
+ * bytes per output element.  Host-only: enqueues nothing.  A negative
+ * status (ULYS_EINVAL) if an argument is < 1.
  */
 int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units);
 
@@ -325,16 +328,12 @@ int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units);
  * their log-sum-exp).
  *
  * Returns the run count R > 0 that ulys_attend_group uses for (batch,
- * q_rows, kv_rows) on compute_units CUs when ulys_attend_splits gives 1, else
- * 0 (no range split).  Candidates are the multiples of compute_units / 8
- * above the query tiles T = ceil(q_rows / 256) and up to 2T; the R minimising
- * a model of the launch time averaged over calls of 2, 4, 8, 10 and 16 heads
- * is taken if it beats no split by 3%.  The model: a round of a <= cus
- * one-tile workgroups takes max(0.74, (a / cus)^0.35) of a full round (the
- * device's throughput grows as the 0.65th power of its busy CUs); a run does
- * T / R of a key sweep plus two pieces' start-up of six key tiles; the merge
- * moves 18 bytes per output element.  Host-only: enqueues nothing.  A
- * negative status (ULYS_EINVAL) if an argument is < 1.
+ * q_rows, kv_rows) on compute_units CUs, or 0 when the same model (see
+ * ulys_attend_splits) chooses no split or a key-range split.  Candidates are
+ * the multiples of compute_units / 8 above the query tiles
+ * T = ceil(q_rows / 256) and up to 4T; a range does T / R of a key sweep plus
+ * two pieces' start-up.  Host-only: enqueues nothing.  A negative status
+ * (ULYS_EINVAL) if an argument is < 1.
  */
 int ulys_attend_ranges(int batch, int q_rows, int kv_rows, int compute_units);
 

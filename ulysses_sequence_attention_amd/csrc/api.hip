@@ -101,104 +101,72 @@ int hip_status(hipError_t e) {
   return fail(ULYS_EHIP, "HIP: %s", hipGetErrorString(e));
 }
 
-// Automatic key-range split of an attention call: the run count C that
-// minimises a model of the launch time, averaged over calls of 2, 4, 8 and 16
-// heads (the head counts of pipeline groups; the choice must not depend on the
-// head count, so that a call over a subset of the heads reproduces the full
-// call's bytes), kept only if it beats no split by 3%.  Model, in units of one
-// workgroup's time over all keys (measured on MI355X: a 2-head call at the
-// 27280-row shape runs 4% slower with 2 or 7 runs, a 10-head call 7% faster
-// with 2 or 4 runs):
-//  * workgroups run in rounds of one per CU, but the device's throughput
-//    saturates at about 84% of its CUs busy (the clock drops as more CUs
-//    work), so a full round takes 1/0.84 of a partly filled one;
-//  * a run costs 1/C of the keys plus about six key tiles of start-up
-//    (Q load, pipeline fill, partial write);
-//  * the merge moves 4C + 2 bytes per output element at an HBM rate of 1.25
-//    times the per-CU attention rate in bytes per flop.
-int auto_splits(long long batch, long long q_rows, long long kv_rows, int cus) {
-  const double units = (double)batch * ((q_rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup);
-  const double nt = (double)((kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile);
-  const double kSaturation = 0.84, kStartTiles = 6.0, kMinTilesPerChunk = 16.0, kGain = 0.97;
-  const double n_sat = kSaturation * cus;
-  auto cost = [&](int c, int hq) {
-    const double wgs = units * c * hq;
-    const double full = floor(wgs / cus), rest = wgs - full * cus;
-    const double per = 1.0 / c + kStartTiles / nt;
-    double t = full * (cus / n_sat) * per;
-    if (rest > 0) t += per * fmax(1.0, rest / n_sat);
-    if (c > 1) t += hq * units * (4.0 * c + 2.0) / (320.0 * nt);
-    return t;
-  };
-  static const int kHeads[] = {2, 4, 8, 16};
-  int best = 1;
-  double best_cost = 1.0;
-  for (int c = 2; c <= ulys::kMaxKeySplits && nt >= c * kMinTilesPerChunk; ++c) {
-    double rel = 0.0;
-    for (int hq : kHeads) rel += cost(c, hq) / cost(1, hq);
-    rel /= (double)(sizeof kHeads / sizeof kHeads[0]);
-    if (rel < kGain * best_cost) {
-      best = c;
-      best_cost = rel;
-    }
-  }
-  return best;
-}
+// Automatic split of an attention call: none, a key-range split into C runs
+// per query tile, or a range split into R runs per (b, head), whichever
+// minimises one model of the launch time averaged over calls of 2, 4, 8, 10
+// and 16 heads (the choice must not depend on the head count, so that a call
+// over a subset of the heads reproduces the full call's bytes), kept only if
+// it beats no split by 3%.  Candidates: C in [2, 16] with at least 16 key
+// tiles per run; R a multiple of cus / 8 above the query tiles T and up to
+// 4T (and 32T, 4096).  Model, in units of one workgroup's sweep over all
+// keys (fitted to 45 MI355X measurements of C and R splits at 1500 to 75600
+// rows and 2 to 10 heads, D = 128: 2.2% rms error in the speed-up):
+//  * workgroups run in rounds of one per CU; a round of a workgroups takes
+//    max(0.8, (a / cus)^0.25) of a full one (the device's throughput grows
+//    only as the 0.75th power of its busy CUs, with a floor);
+//  * a workgroup's share of the keys (1/C, or T/R of a sweep) plus eight key
+//    tiles of start-up per piece (one for a key-range run, two for a range);
+//  * the merge moves 4C + 2 (C split) or 18 (range split) bytes per output
+//    element at 1280 times the per-CU attention rate in bytes per flop.
+struct SplitChoice {
+  int c;   // key-range runs per query tile (1: none)
+  int r;   // range runs per (b, head) (0: none)
+};
 
-// Automatic range split of a call that auto_splits leaves unsplit: R equal
-// runs of each (b, head)'s (query tile, key tile) sequence, so that the
-// workgroups fill whole rounds of CUs with less than one query tile each.
-// Candidates: multiples of cus / 8 between the query tiles and twice them;
-// the R that minimises the modelled time averaged over 2, 4, 8, 10 and 16
-// heads (independent of the head count, as for C), kept only if it beats no
-// split by 3%; 0 = none.  Model (fitted to MI355X launches of 128, 214 and
-// 256 one-tile workgroups at the 27280-key shape, and to 10-head calls):
-//  * a round of a workgroups (a <= cus, one per CU) takes
-//    max(0.74, (a / cus)^0.35) of a full round: the device's throughput grows
-//    only as the 0.65th power of the busy CUs, with a floor for small rounds;
-//  * a range does qtiles / R of a key sweep plus two pieces' start-up (six
-//    key tiles each);
-//  * the merge moves 18 bytes per output element (two fp32 pieces written
-//    and read, one bf16 write), priced as for the key-range split.
-int auto_ranges(long long batch, long long q_rows, long long kv_rows, int cus) {
+SplitChoice auto_split(long long batch, long long q_rows, long long kv_rows, int cus) {
   const long long qt = (q_rows + ulys::kAttnRowsPerWorkgroup - 1) / ulys::kAttnRowsPerWorkgroup;
   const double nt = (double)((kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile);
-  const double kFloor = 0.74, kExp = 0.35, kStartTiles = 6.0, kGain = 0.97;
+  const double units = (double)batch * (double)qt;
+  const double kExp = 0.25, kFloor = 0.8, kStartTiles = 8.0, kMergeRate = 1.0 / 1280.0, kGain = 0.97;
+  const double kMinTilesPerChunk = 16.0;
   auto rounds = [&](double wgs, double per) {
     const double full = floor(wgs / cus), rest = wgs - full * cus;
     return per * (full + (rest > 0 ? fmax(kFloor, pow(rest / cus, kExp)) : 0.0));
   };
+  auto plain = [&](int hq) { return rounds(units * hq, 1.0); };
+  auto cost_c = [&](int c, int hq) {
+    return rounds(units * c * hq, 1.0 / c + kStartTiles / nt) + hq * units * (4.0 * c + 2.0) * kMergeRate / nt;
+  };
+  auto cost_r = [&](long long r, int hq) {
+    return rounds((double)batch * r * hq, (double)qt / (double)r + 2.0 * kStartTiles / nt) +
+           hq * units * 18.0 * kMergeRate / nt;
+  };
   static const int kHeads[] = {2, 4, 8, 10, 16};
   constexpr int kNH = sizeof kHeads / sizeof kHeads[0];
-  const long long step = cus >= 8 ? cus / 8 : 1;
-  const long long rmax = std::min<long long>(std::min<long long>(2 * qt, ulys::kMaxRanges),
-                                             (long long)ulys::kMaxRangesPerTile * qt);
-  int best = 0;
+  SplitChoice best{1, 0};
   double best_rel = kGain;
-  for (long long r = (qt / step + 1) * step; r <= rmax; r += step) {
+  for (int c = 2; c <= ulys::kMaxKeySplits && nt >= c * kMinTilesPerChunk; ++c) {
     double rel = 0.0;
-    for (int hq : kHeads) {
-      const double plain = rounds((double)batch * qt * hq, 1.0);
-      const double per = (double)qt / (double)r + 2.0 * kStartTiles / nt;
-      const double merge = hq * (double)batch * qt * 18.0 / (320.0 * nt);
-      rel += (rounds((double)batch * r * hq, per) + merge) / plain;
-    }
+    for (int hq : kHeads) rel += cost_c(c, hq) / plain(hq);
     rel /= kNH;
     if (rel < best_rel) {
-      best = (int)r;
+      best = SplitChoice{c, 0};
+      best_rel = rel;
+    }
+  }
+  const long long step = cus >= 8 ? cus / 8 : 1;
+  const long long rmax = std::min<long long>(std::min<long long>(4 * qt, ulys::kMaxRanges),
+                                             (long long)ulys::kMaxRangesPerTile * qt);
+  for (long long r = (qt / step + 1) * step; r <= rmax; r += step) {
+    double rel = 0.0;
+    for (int hq : kHeads) rel += cost_r(r, hq) / plain(hq);
+    rel /= kNH;
+    if (rel < best_rel) {
+      best = SplitChoice{1, (int)r};
       best_rel = rel;
     }
   }
   return best;
-}
-
-// The automatic key_splits value: C > 1 (key-range split), -R (range split)
-// or 1 (none).
-int auto_key_splits(long long batch, long long q_rows, long long kv_rows, int cus) {
-  const int c = auto_splits(batch, q_rows, kv_rows, cus);
-  if (c > 1) return c;
-  const int r = auto_ranges(batch, q_rows, kv_rows, cus);
-  return r > 0 ? -r : 1;
 }
 
 // Compute units of the current device (cached per device).
@@ -346,11 +314,9 @@ int resolve_splits(ulys::AttnArgs& a) {
   int cus = 0;
   const int st = device_cus(&cus);
   if (st) return st;
-  a.splits = auto_key_splits(a.batch, a.q_rows, a.kv_rows, cus);
-  if (a.splits < 0) {
-    a.ranges = -a.splits;
-    a.splits = 1;
-  }
+  const SplitChoice ch = auto_split(a.batch, a.q_rows, a.kv_rows, cus);
+  a.splits = ch.c;
+  a.ranges = ch.r;
   return ULYS_OK;
 }
 
@@ -565,15 +531,14 @@ int ulys_attend_splits(int batch, int q_rows, int kv_rows, int compute_units) {
   if (batch < 1 || q_rows < 1 || kv_rows < 1 || compute_units < 1)
     return fail(ULYS_EINVAL, "batch, q_rows, kv_rows and compute_units must be >= 1");
   ok();
-  return auto_splits(batch, q_rows, kv_rows, compute_units);
+  return auto_split(batch, q_rows, kv_rows, compute_units).c;
 }
 
 int ulys_attend_ranges(int batch, int q_rows, int kv_rows, int compute_units) {
   if (batch < 1 || q_rows < 1 || kv_rows < 1 || compute_units < 1)
     return fail(ULYS_EINVAL, "batch, q_rows, kv_rows and compute_units must be >= 1");
   ok();
-  return auto_splits(batch, q_rows, kv_rows, compute_units) > 1 ? 0
-                                                               : auto_ranges(batch, q_rows, kv_rows, compute_units);
+  return auto_split(batch, q_rows, kv_rows, compute_units).r;
 }
 
 int ulys_auto_groups(const ulys_layout* L, int compute_units) {
@@ -589,11 +554,11 @@ int ulys_auto_groups(const ulys_layout* L, int compute_units) {
                          (long long)L->degree * L->s_local;
   const long long hq_rank = L->hq / L->degree, hkv_rank = L->hkv / L->degree;
   // Workgroups of the one-call attention (256 query rows each, times the
-  // automatic key-range split, which is the same for every group count; one
-  // per CU at a time) and the rounds of CUs they take.
-  const long long ks = auto_key_splits(L->batch, rows, rows_kv, compute_units);
-  const long long per_head = ks < 0 ? -ks : ks * ((rows + ulys::kAttnRowsPerWorkgroup - 1) /
-                                                  ulys::kAttnRowsPerWorkgroup);
+  // automatic key-range split, or the range split's runs; the same for every
+  // group count; one per CU at a time) and the rounds of CUs they take.
+  const SplitChoice ch = auto_split(L->batch, rows, rows_kv, compute_units);
+  const long long per_head = ch.r > 0 ? ch.r : (long long)ch.c * ((rows + ulys::kAttnRowsPerWorkgroup - 1) /
+                                                                   ulys::kAttnRowsPerWorkgroup);
   const long long wgs = (long long)L->batch * hq_rank * per_head;
   const long long rounds_one = (wgs + compute_units - 1) / compute_units;
   static const int kCandidates[] = {7, 5, 4, 3, 2};
