@@ -308,7 +308,7 @@ int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, in
  * Returns the run count C >= 1 that ulys_attend_group uses for
  * (batch, q_rows, kv_rows) on a device with compute_units CUs (1: no
  * key-range split).  One model chooses among no split, C in [2, 16] (each
- * run >= 16 key tiles) and the range split of ulys_attend_ranges: the choice
+ * run >= 4 key tiles) and the range split of ulys_attend_ranges: the choice
  * minimising the modelled launch time averaged over calls of 2, 4, 8, 10 and
  * 16 heads, if it beats no split by 3%.  The model: workgroups run in rounds
  * of one per CU and a round of a workgroups takes max(0.8, (a / cus)^0.25)

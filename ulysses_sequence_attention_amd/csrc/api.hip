@@ -106,7 +106,7 @@ int hip_status(hipError_t e) {
 // minimises one model of the launch time averaged over calls of 2, 4, 8, 10
 // and 16 heads (the choice must not depend on the head count, so that a call
 // over a subset of the heads reproduces the full call's bytes), kept only if
-// it beats no split by 3%.  Candidates: C in [2, 16] with at least 16 key
+// it beats no split by 3%.  Candidates: C in [2, 16] with at least 4 key
 // tiles per run; R a multiple of cus / 8 above the query tiles T and up to
 // 4T (and 32T, 4096).  Model, in units of one workgroup's sweep over all
 // keys (fitted to 45 MI355X measurements of C and R splits at 1500 to 75600
@@ -128,7 +128,7 @@ SplitChoice auto_split(long long batch, long long q_rows, long long kv_rows, int
   const double nt = (double)((kv_rows + ulys::kAttnKeysPerTile - 1) / ulys::kAttnKeysPerTile);
   const double units = (double)batch * (double)qt;
   const double kExp = 0.25, kFloor = 0.8, kStartTiles = 8.0, kMergeRate = 1.0 / 1280.0, kGain = 0.97;
-  const double kMinTilesPerChunk = 16.0;
+  const double kMinTilesPerChunk = 4.0;
   auto rounds = [&](double wgs, double per) {
     const double full = floor(wgs / cus), rest = wgs - full * cus;
     return per * (full + (rest > 0 ? fmax(kFloor, pow(rest / cus, kExp)) : 0.0));
