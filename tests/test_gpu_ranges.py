@@ -173,3 +173,18 @@ def test_automatic_ranges_is_the_reported_one(gpu):
     torch.cuda.synchronize()
     assert r > 0
     assert _same((o, l), _run(gpu, qd, kd, vd, r))
+
+
+def test_ranges_heads_in_several_launches(gpu):
+    """4096 runs over 128 query tiles need 1.03 GB of partials per head, so the 2 GiB workspace
+    takes one head per launch: 3 launches, each head as in a one-head call."""
+    b, n, hq, d, ranges = 1, 32768, 3, 128, 4096
+    q, k, v = _qkv(1200, b, n, n, hq, 1, d)
+    qd, kd, vd = from_bits(q), from_bits(k), from_bits(v)
+    o, l = _run(gpu, qd, kd, vd, ranges)
+    rows = sample_rows(n, boundaries=(256, n - 200), extra=16)
+    o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(d), rows=rows)
+    check_attention(o, l, o_ref, l_ref, rows=rows, label="3 launches")
+    o1, l1 = _run(gpu, qd[:, :, 2:3].contiguous(), kd, vd, ranges)
+    assert torch.equal(o1.view(torch.int16), o[:, :, 2:3].contiguous().view(torch.int16))
+    assert torch.equal(l1, l[:, 2:3].contiguous())
