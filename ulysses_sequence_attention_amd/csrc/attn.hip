@@ -749,7 +749,7 @@ void attn_fwd_kernel(AttnArgs a) {
                   __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
         // the next step reads K from the stage after SB
         const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
         tile_barrier();
         return true;
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(AttnArgs a) 
         const float w = __builtin_amdgcn_exp2f(lv[s] - mx);   // 0 for an empty split
         const f32x4* src = (const f32x4*)(a.part_o + s * split_o + rh * D + 8 * c);
         const f32x4 x0 = __builtin_nontemporal_load(src), x1 = __builtin_nontemporal_load(src + 1);
-        #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[i] += w * x0[i];
           acc[4 + i] += w * x1[i];
