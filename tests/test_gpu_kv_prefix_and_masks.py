@@ -154,7 +154,8 @@ def test_random_key_masks(gpu, case):
     check_attention(o, l, o_ref, l_ref, label=f"mask {case}")
 
 
-@pytest.mark.parametrize("pattern", ["tiles", "alternate", "tail", "head", "one_key", "gap_and_mask"])
+@pytest.mark.parametrize("pattern", ["tiles", "alternate", "tail", "head", "one_key", "gap_and_mask",
+                                     "gap_in_full_mask"])
 def test_masks_that_skip_tiles(gpu, pattern):
     """Masks that leave whole 64-key tiles empty (the tile list skips them) or single keys."""
     b, nq, nk, h, d = 1, 200, 1100, 2, 128
@@ -178,6 +179,9 @@ def test_masks_that_skip_tiles(gpu, pattern):
         m[:, 777] = True
     elif pattern == "gap_and_mask":
         m = inputs.random_key_mask(b, nk, 54, 0.6)
+        gaps = [(300, 700)]
+    elif pattern == "gap_in_full_mask":   # mask words all ones where the gap cuts tiles 4 and 10
+        m[:, 900:960] = False
         gaps = [(300, 700)]
     o, l = _attend_ex(gpu, from_bits(q), from_bits(k), from_bits(v), gaps=gaps, mask=m)
     o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(d), gaps, key_mask=m)
