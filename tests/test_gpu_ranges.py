@@ -188,3 +188,24 @@ def test_ranges_heads_in_several_launches(gpu):
     o1, l1 = _run(gpu, qd[:, :, 2:3].contiguous(), kd, vd, ranges)
     assert torch.equal(o1.view(torch.int16), o[:, :, 2:3].contiguous().view(torch.int16))
     assert torch.equal(l1, l[:, 2:3].contiguous())
+
+
+def test_ranges_gqa_mask_fp8_d64(gpu):
+    """GQA 4:1, head_dim 64, e4m3 q/k and a key mask with per-batch tile counts, in 11 runs."""
+    b, nq, nk, hq, hkv, d, ranges = 3, 700, 2600, 4, 1, 64, 11
+    q = inputs.random_bf16((b, nq, hq, d), 1210).float().numpy()
+    k = inputs.random_bf16((b, nk, hkv, d), 1211).float().numpy()
+    v = inputs.random_bf16((b, nk, hkv, d), 1212)
+    mask = inputs.random_key_mask(b, nk, seed=1213, p_valid=0.5)
+    mask[1, 700:2400] = False
+    mask[2, :64] = False
+    aq, ak = ofp8.amax([q]), ofp8.amax([k])
+    sq, iq = ofp8.scales_from_amax(aq)
+    sk, ik = ofp8.scales_from_amax(ak)
+    qc, kc = ofp8.quantize(q, iq), ofp8.quantize(k, ik)
+    amax = torch.tensor([aq, ak], dtype=torch.float32, device="cuda")
+    o, l = _run(gpu, torch.from_numpy(qc).cuda(), torch.from_numpy(kc).cuda(), v.cuda(), ranges, mask=mask,
+                fp8=True, amax=amax)
+    c = ofp8.score_scale(oatt.default_scale(d), sq, sk)
+    o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), v.double().numpy(), float(c), key_mask=mask)
+    check_attention(o, l, o_ref, l_ref, label="GQA fp8 mask ranges 11")
