@@ -41,6 +41,11 @@
 //    MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
+//  * Work per workgroup: one query tile over all its key tiles; or, under a
+//    key-range split, a contiguous run of them; or, under a range split, a
+//    run of its (b, h)'s (query tile, key tile) sequence, walked as pieces.
+//    A tile computed in parts leaves fp32 partials (o, lse) that a second
+//    kernel merges in a fixed order (split_merge_kernel, range_merge_kernel).
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
 #include <algorithm>
