@@ -314,3 +314,22 @@ def test_key_mask_word_encoding():
         for j in range(128):
             bit = (int(w[b, j // 32]) >> (j % 32)) & 1
             assert bit == (int(m[b, j]) if j < 100 else 0)
+
+
+def test_split_choice_invariants(U):
+    """Over seeded random shapes and CU counts: the automatic key-range runs C and range runs R are
+    never both taken, C has at least 4 key tiles per run, and R is a multiple of cus/8 in (T, 4T]."""
+    import random
+    rng = random.Random(7)
+    for _ in range(400):
+        batch = rng.choice([1, 1, 2, 3, 8])
+        q_rows = rng.randint(1, 120000)
+        kv_rows = rng.choice([q_rows, rng.randint(1, 200000)])
+        cus = rng.choice([80, 256, 304])
+        c = U.ulys_attend_splits(batch, q_rows, kv_rows, cus)
+        r = U.ulys_attend_ranges(batch, q_rows, kv_rows, cus)
+        qt, nt = (q_rows + 255) // 256, (kv_rows + 63) // 64
+        assert 1 <= c <= 16 and r >= 0
+        assert c == 1 or r == 0
+        assert c == 1 or nt >= 4 * c
+        assert r == 0 or (r % (cus // 8) == 0 and qt < r <= min(4 * qt, 32 * qt, 4096))
