@@ -9,8 +9,9 @@ repack does not re-read one rank's bytes from cache.
 
 `value` = attention TFLOP/s of the whole step (4*N^2*D*heads per step over
 the step time, pack and unpack included).  The JSON line also carries the
-attention kernel's own rate (`roofline`, HIP events around each launch on the
-launch stream), the repack GB/s, the same steps under the two-stream group
+attention launch's own rate (`roofline`: HIP events around each launch on the
+launch stream; a launch is the attention kernel plus, under the automatic
+range split, its merge kernel), the repack GB/s, the same steps under the two-stream group
 pipeline (ulys_rank_pipeline; `--pipeline` times that one instead), a plain
 device copy rate, and the CPU oracle timed on a bounded sample
 (`cpu_baseline`).
