@@ -9,7 +9,10 @@
  * plus ulys_rank_pipeline (the three steps for every head group of a rank,
  * repack overlapping attention on a second stream), ulys_lse_merge (merge of
  * partial results over key blocks, for ring / hybrid parallelism), ulys_amax_bf16
- * (per-tensor fp8 scale source), ulys_strerror and ulys_last_error.
+ * (per-tensor fp8 scale source), ulys_attend_group_ex (different query and key
+ * lengths, key masks, an explicit work split), ulys_attend_splits /
+ * ulys_attend_ranges / ulys_auto_groups (the automatic choices, host-only),
+ * ulys_strerror and ulys_last_error.
  *
  * Conventions shared by every call
  *   - Tensors are caller-owned device memory, dense, row-major, with the
