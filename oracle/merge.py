@@ -1,17 +1,15 @@
 """Oracle: merging partial attention results over key blocks by their LSE -- test infrastructure.
 
-What is merged (flashdreams ``core/attention/cp.py``,
-``ContextParallelAttention._impl_ring``): each step attends the local
-queries to one block of keys and returns ``(out, lse)``; the running result
-``(prev_out, prev_lse)`` absorbs it as
-
-    w       = sigmoid(lse - prev_lse)
-    out     = prev_out - w * (prev_out - out)
-    lse     = prev_lse - logsigmoid(prev_lse - lse)
-
-(optionally in float32: ``convert_to_fp32``).  Blocks are absorbed in the
-order given.  Here every step runs in float64 on the exact values the
-kernel reads (bf16 outputs widened, float32 LSEs widened).
+What is merged (flashdreams ``core/attention/cp.py``, ``ContextParallelAttention``,
+ring path): every ring step attends the local queries to one block of keys and
+yields an output and its log-sum-exp.  The running result takes in each new
+block in turn: the new block's share of the weight is the logistic function of
+its LSE minus the running LSE, the running output moves towards the block's
+output by that share, and the running LSE becomes the log of the sum of the two
+exponentials (written with the log-logistic function, which stays finite for
+large LSE gaps).  The page can do this in float32; here every step runs in
+float64 on the exact values the kernel reads (bf16 outputs widened, float32
+LSEs widened), blocks in the order given.
 
 A block whose LSE is -inf (no valid key in it) has weight 0.  The merged
 result is attention over the union of the blocks' keys; that, not this

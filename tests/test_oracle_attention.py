@@ -125,8 +125,8 @@ def test_invariants():
 
 
 def test_ring_lse_merge_equals_full():
-    """flashdreams _impl_ring: merging (out, lse) of two disjoint key blocks with
-    out = prev - sigmoid(lse - prev_lse) * (prev - out), lse = prev_lse - logsigmoid(prev_lse - lse)
+    """flashdreams cp.py, ring path: taking in the second block's (out, lse) with the logistic
+    weight of the LSE difference, and the LSE as the log of the two summed exponentials,
     reproduces attention over all keys."""
     b, n, h, d = 1, 30, 2, 8
     q, k, v = _rand((b, n, h, d), 16), _rand((b, 2 * n, h, d), 17), _rand((b, 2 * n, h, d), 18)
@@ -249,3 +249,23 @@ def test_all_masked_batch_gives_zero_and_neg_inf():
     ob, lseb = brute.attention(q.tolist(), k.tolist(), v.tolist(), 0.5, key_mask=m.tolist())
     assert np.all(np.array(ob)[1] == 0) and np.all(np.isneginf(np.array(lseb)[1]))
     assert np.all(np.isfinite(lse[0]))
+
+
+@pytest.mark.parametrize("d", [64, 128, 96, 8])
+def test_default_scale_is_head_dim_inverse_sqrt(d):
+    """sglang layer.py, UlyssesAttention / USPAttention: the softmax scale defaults to head_size**-0.5.
+    The oracle passes it to the kernel as a float32; torch's SDPA uses the same default
+    (1/sqrt(E) for scale=None), so attention with default_scale matches SDPA's own default to the
+    float32 rounding of the scale (exactly when d is a power of 4)."""
+    c = oa.default_scale(d)
+    assert c == float(np.float32(d ** -0.5))
+    assert abs(c - 1.0 / np.sqrt(d)) <= 2.0 ** -24 / np.sqrt(d)
+    q, k, v = _rand((1, 20, 2, d), 30), _rand((1, 20, 2, d), 31), _rand((1, 20, 2, d), 32)
+    o, _ = oa.attention(q, k, v, c)
+    qt, kt, vt = (torch.from_numpy(x).transpose(1, 2) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).transpose(1, 2).numpy()
+    tol = 1e-12 if d in (64, 16, 4) else 1e-6
+    assert np.allclose(o, ref, rtol=0, atol=tol)
+    # a planted mistake (1/d instead of 1/sqrt(d)) is visibly different
+    o_bad, _ = oa.attention(q, k, v, 1.0 / d)
+    assert not np.allclose(o_bad, ref, rtol=0, atol=1e-3)
