@@ -11,8 +11,9 @@
  * partial results over key blocks, for ring / hybrid parallelism), ulys_amax_bf16
  * (per-tensor fp8 scale source), ulys_attend_group_ex (different query and key
  * lengths, key masks, an explicit work split), ulys_attend_splits /
- * ulys_attend_ranges / ulys_auto_groups (the automatic choices, host-only),
- * ulys_strerror and ulys_last_error.
+ * ulys_attend_ranges / ulys_auto_groups / ulys_attend_workspace_bytes (the
+ * automatic choices and the workspace size, host-only), ulys_strerror and
+ * ulys_last_error.
  *
  * Conventions shared by every call
  *   - Tensors are caller-owned device memory, dense, row-major, with the
@@ -22,7 +23,11 @@
  *     call; the caller may reuse them on return.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work on it; none synchronises, allocates device memory, or keeps state
- *     between calls.
+ *     between calls.  Scratch memory (the attention workspace) and the
+ *     pipeline's events are the caller's, passed in like the tensors
+ *     (sglang PR #43521, "Buffers": the caller's pool holds every buffer of
+ *     the path).  The only state is the text behind ulys_last_error and a
+ *     cache of each device's compute-unit count.
  *   - All validation happens before anything is enqueued.  On failure the
  *     call returns a negative ulys_status, enqueues nothing, and
  *     ulys_last_error() describes the first violated rule.
@@ -145,12 +150,12 @@ int ulys_pack(const ulys_layout* layout, int rank, int group,
  * ulys_lse_merge -- merge the partial results of attention over disjoint key
  * blocks into the result over all of them.
  *
- * Source: flashdreams cp.py, ContextParallelAttention._impl_ring (ring
- * attention over the CP ranks' key blocks: each step's (out, lse) is absorbed
- * with out = prev - sigmoid(lse - prev_lse) * (prev - out) and
- * lse = prev_lse - logsigmoid(prev_lse - lse), in float32 when
- * convert_to_fp32); the Ulysses + ring hybrid of sglang's USPAttention uses
- * the same merge across its ring dimension.
+ * Source: flashdreams cp.py, ContextParallelAttention, ring path (ring
+ * attention over the CP ranks' key blocks: the running result takes in each
+ * step's output with a logistic weight of the LSE difference and its LSE
+ * becomes the log of the summed exponentials, optionally in float32); the
+ * Ulysses + ring hybrid of sglang's USPAttention uses the same merge across
+ * its ring dimension.
  *
  * For every b, head h, row i:  L = ln sum_p exp(lse_p),
  *   o_out = sum_p exp(lse_p - L) * o_p,  lse_out = L
@@ -198,6 +203,13 @@ int ulys_auto_groups(const ulys_layout* layout, int compute_units);
  * ulys_amax_bf16 -- amax_out[0] = max |x| over n_tensors bf16 device arrays
  * of elems_each elements each (the per-tensor fp8 scale source; exact,
  * independent of order).  amax_out is a device float, overwritten.
+ *
+ * Source: LightX2V PR "Add optimized Ulysses attention path", review of the
+ * fp8 communication records (the fp8 payload and its scale travel as two
+ * tensors, and the receiver dequantises with the scale); the pages give no
+ * scale formula, and this library reads it as one scale per tensor over all
+ * shards, amax / 448 (the largest e4m3fn magnitude), so that the largest
+ * element maps to the largest code.
  * Rules: n_tensors >= 1, every pointer non-NULL and 16-byte aligned,
  * elems_each a multiple of 8 (ULYS_EINVAL otherwise).
  */
@@ -240,11 +252,16 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * its 64-key tiles, each writing an fp32 partial (o, lse); a second kernel
  * combines them in run order with the log-sum-exp weights.  C depends on
  * (batch, rows, the device's compute units) only, so the head-subset rule
- * above still holds.  The partials live in a device workspace that the
- * library allocates per (device, stream) on first use and keeps (up to
- * 2 GiB, or one head's partials when those alone need more; a call needing
- * more runs its heads in several launches); calls on one stream share it in
- * stream order.
+ * above still holds.
+ *
+ * Workspace: the partials of a split live in `workspace`, caller-owned
+ * device memory of `workspace_bytes` bytes, 256-byte aligned.
+ * ulys_attend_workspace_bytes gives the size for all heads in one launch (0
+ * when the call takes no split; then workspace may be NULL).  A smaller
+ * workspace that still holds one head's partials (the size for heads = 1)
+ * runs the heads in several launches, with the same bytes; below that the
+ * call is ULYS_EINVAL.  The call overwrites the workspace; calls that share
+ * one must be ordered (one stream, or events).
  *
  * Range split (automatic, see ulys_attend_ranges): the (query
  * tile, key tile) pairs of each (b, head), taken query tile by query tile,
@@ -253,12 +270,14 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
  * query tile inside one run is written directly; the pieces of a tile cut
  * by run ends write fp32 partials (same workspace) that a second kernel
  * combines in run order with the log-sum-exp weights.  R depends on (batch,
- * rows, compute units) only, so the head-subset rule holds here too.
+ * rows, compute units) only, so the head-subset rule holds here too.  Its
+ * partials live in the same workspace.
  */
 int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       const void* q, const void* k, const void* v, int qk_dtype,
                       float softmax_scale, const float* qk_amax,
-                      const int32_t* key_gaps, void* o, float* lse, void* stream);
+                      const int32_t* key_gaps, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ulys_attend_group_ex -- ulys_attend_group with query and key sequences of
@@ -291,13 +310,35 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  * ulys_attend_group(B, rows, ...) equals ulys_attend_group_ex(B, rows, rows,
  * ..., key_mask = NULL, key_splits = 0, ...), and a mask that marks exactly
  * the keys outside the gaps gives the same bytes as the gaps (at equal
- * key_splits).
+ * key_splits).  workspace / workspace_bytes as for ulys_attend_group (sized
+ * by ulys_attend_workspace_bytes with the same key_splits).
  */
 int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim,
                          const void* q, const void* k, const void* v, int qk_dtype,
                          float softmax_scale, const float* qk_amax,
                          const int32_t* key_gaps, const uint32_t* key_mask, int key_splits,
-                         void* o, float* lse, void* stream);
+                         void* o, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * ulys_attend_workspace_bytes -- device workspace bytes that an attention call
+ * of this shape needs for all `heads` of it in one launch.
+ *
+ * Source: sglang PR #43521, "Buffers" (the caller's pool holds every buffer
+ * of the attention path, sized once per shape); the workspace holds the
+ * partial results of a split launch (ulys_attend_group), combined by their
+ * log-sum-exp as in flashdreams cp.py, ContextParallelAttention, ring path.
+ *
+ * key_splits as for ulys_attend_group_ex (0 = the automatic choice, which
+ * depends on compute_units: pass the device's compute-unit count,
+ * hipDeviceAttributeMultiprocessorCount).  Returns the byte count (>= 0; 0:
+ * no split, no workspace), or a negative ulys_status: ULYS_EINVAL if an
+ * argument is < 1 or key_splits is out of range, ULYS_EUNSUPPORTED for
+ * head_dim not 64/128.  Host-only: enqueues nothing.  With heads = 1 it
+ * gives the smallest workspace the call accepts.
+ */
+long long ulys_attend_workspace_bytes(int batch, int q_rows, int kv_rows, int heads, int head_dim,
+                                      int key_splits, int compute_units);
 
 /*
  * ulys_attend_splits -- the automatic key-range split of an attention call.
@@ -384,8 +425,15 @@ int ulys_unpack(const ulys_layout* layout, int rank, int group,
  * `stream` after the call after the last unpack, so the caller synchronises
  * on `stream` alone.  Passing the same stream twice runs everything in order
  * on it.  Every rule of the three calls is checked before anything is
- * enqueued; G <= 64 (ULYS_EUNSUPPORTED otherwise).  The call creates 2G + 2
- * HIP events and releases them before returning (ULYS_EHIP if creation fails).
+ * enqueued; G <= 64 (ULYS_EUNSUPPORTED otherwise).
+ *
+ * events: host array of 3 hipEvent_t that the caller created (any flags;
+ * hipEventDisableTiming is the cheapest) and owns; the call records them on
+ * the two streams and makes each stream wait on them (a stream wait takes the
+ * event's state when it is enqueued), and creates or destroys none, so the
+ * same three may serve every call.  workspace / workspace_bytes: the
+ * attention workspace (ulys_attend_group) for Gq heads at
+ * (B, rows_q, rows_kv), shared by the G attention launches in stream order.
  */
 int ulys_rank_pipeline(const ulys_layout* layout, int rank,
                        const void* const* q_shards, const void* const* k_shards,
@@ -393,7 +441,9 @@ int ulys_rank_pipeline(const ulys_layout* layout, int rank,
                        void* q_slots, void* k_slots, void* v_slots, void* o_slots,
                        float* lse, void* const* o_shards,
                        int qk_dtype, const float* qk_amax, float softmax_scale,
-                       const int32_t* key_gaps, void* stream, void* copy_stream);
+                       const int32_t* key_gaps, void* const* events,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream, void* copy_stream);
 
 /* Static text for a ulys_status value. */
 const char* ulys_strerror(int status);

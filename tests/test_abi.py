@@ -23,13 +23,13 @@ def U():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(ulys_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+long|\w+)\*?\s+\*?(ulys_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_path():
     names = _declared()
     for n in ("ulys_pack", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits", "ulys_unpack",
-              "ulys_rank_pipeline",
+              "ulys_rank_pipeline", "ulys_attend_workspace_bytes",
               "ulys_lse_merge", "ulys_auto_groups", "ulys_amax_bf16", "ulys_strerror", "ulys_last_error"):
         assert n in names
 
@@ -100,7 +100,7 @@ def _attend(U, batch=1, rows=100, hq=2, hkv=2, d=128, q=FAKE, o=FAKE, dtype=0, s
     if gaps is not None:
         g = (ctypes.c_int32 * len(gaps))(*gaps)
     return U.call_raw("ulys_attend_group", batch, rows, hq, hkv, d, q, FAKE, FAKE, dtype, ctypes.c_float(scale),
-                      amax, g, o, lse, None)
+                      amax, g, o, lse, None, 0, None)
 
 
 def test_attend_rules(U):
@@ -123,12 +123,13 @@ def test_attend_rules(U):
     assert _attend(U, batch=300, gaps=[0, 1] * 300) == -1             # too many gap batches
 
 
-def _attend_ex(U, batch=1, nq=100, nk=140, hq=2, hkv=2, d=128, dtype=0, gaps=None, mask=None, splits=0):
+def _attend_ex(U, batch=1, nq=100, nk=140, hq=2, hkv=2, d=128, dtype=0, gaps=None, mask=None, splits=0, ws=None,
+               ws_bytes=0):
     g = None
     if gaps is not None:
         g = (ctypes.c_int32 * len(gaps))(*gaps)
     return U.call_raw("ulys_attend_group_ex", batch, nq, nk, hq, hkv, d, FAKE, FAKE, FAKE, dtype, ctypes.c_float(0.0),
-                      None, g, mask, splits, FAKE, None, None)
+                      None, g, mask, splits, FAKE, None, ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_attend_ex_rules(U):
@@ -147,6 +148,44 @@ def test_attend_ex_rules(U):
     assert _attend_ex(U, splits=-33) == -1                             # ranges: at most 32 per query tile
     assert "per query tile" in U.last_error()
     assert _attend_ex(U, nq=257, splits=-65) == -1                     # (2 query tiles: 64 ranges)
+
+
+def _ws_bytes(U, batch, nq, nk, heads, d, splits, cus=256):
+    return U.call_raw("ulys_attend_workspace_bytes", batch, nq, nk, heads, d, splits, cus)
+
+
+def test_workspace_bytes_arithmetic(U):
+    """Workspace of a split call: fp32 partial o (D floats) and lse (one float) per query row and run
+    (key-range split C: every row of every run; range split R: two 256-row tile pieces per run), per
+    head, plus 256 bytes for the per-batch tile counts."""
+    lib = ctypes.CDLL(U.LIB_PATH)
+    lib.ulys_attend_workspace_bytes.restype = ctypes.c_longlong
+    f = lambda *a: lib.ulys_attend_workspace_bytes(*a)
+    assert f(1, 100, 140, 2, 128, 1, 256) == 0                         # no split, no workspace
+    assert f(2, 1000, 3000, 3, 64, 4, 256) == 256 + 3 * 4 * 2 * 1000 * (64 + 1) * 4
+    assert f(1, 27280, 27280, 2, 128, -128, 256) == 256 + 2 * 128 * 2 * 256 * (128 + 1) * 4
+    assert f(1, 27280, 27280, 10, 128, -128, 256) == 256 + 10 * 128 * 2 * 256 * (128 + 1) * 4
+    # the automatic choice at the Wan share on 256 CUs is the range split into 128 runs
+    assert f(1, 27280, 27280, 2, 128, 0, 256) == f(1, 27280, 27280, 2, 128, -128, 256)
+    assert f(1, 1, 1, 1, 128, 0, 0) == -1
+    assert f(1, 1, 1, 1, 96, 0, 1) == -2
+    assert f(1, 1, 1, 1, 128, 17, 1) == -1
+
+
+def test_workspace_rules(U):
+    """A split call needs a workspace of at least one head's partials, 256-byte aligned (explicit splits,
+    so the rule is checked before any HIP call)."""
+    lib = ctypes.CDLL(U.LIB_PATH)
+    lib.ulys_attend_workspace_bytes.restype = ctypes.c_longlong
+    one = lib.ulys_attend_workspace_bytes(1, 100, 140, 1, 128, 2, 256)
+    assert one > 0
+    assert _attend_ex(U, splits=2) == -1                               # no workspace
+    assert "workspace" in U.last_error()
+    assert _attend_ex(U, splits=2, ws=FAKE, ws_bytes=one - 1) == -1    # below one head's partials
+    assert "ulys_attend_workspace_bytes" in U.last_error()
+    assert _attend_ex(U, splits=2, ws=FAKE + 16, ws_bytes=one) == -1   # not 256-byte aligned
+    assert "aligned" in U.last_error()
+    assert _attend_ex(U, splits=-2, ws=FAKE, ws_bytes=100) == -1       # a range split too
 
 
 def test_attend_splits_rule(U):
@@ -209,13 +248,15 @@ def test_unpack_and_amax_rules(U):
     assert U.call_raw("ulys_amax_bf16", _arr(1, MIS), 1, 8, FAKE, None) == -1
 
 
-def _pipeline(U, L, rank=0, slots=(FAKE,) * 4, lse=None, out=None, dtype=0, amax=FAKE, scale=0.0, gaps=None):
+def _pipeline(U, L, rank=0, slots=(FAKE,) * 4, lse=None, out=None, dtype=0, amax=FAKE, scale=0.0, gaps=None,
+              events="fake"):
+    events = _arr(3) if events == "fake" else events
     c = U.Layout(**L).c_struct()
     P = c.degree
     out = _arr(P) if out is None else out
     g = None if gaps is None else (ctypes.c_int32 * len(gaps))(*gaps)
     return U.call_raw("ulys_rank_pipeline", ctypes.byref(c), rank, _arr(P), _arr(P), _arr(P), *slots, lse, out,
-                      dtype, amax, ctypes.c_float(scale), g, None, None)
+                      dtype, amax, ctypes.c_float(scale), g, events, None, ctypes.c_size_t(0), None, None)
 
 
 def test_pipeline_rules(U):
@@ -232,6 +273,9 @@ def test_pipeline_rules(U):
     assert "no valid key" in U.last_error()
     assert _pipeline(U, dict(GOOD, head_dim=96)) == -2
     assert _pipeline(U, dict(GOOD, hq=4 * 65, hkv=4 * 65, groups=65)) == -2   # more than 64 groups
+    assert _pipeline(U, GOOD, events=None) == -1                       # the caller's three events
+    assert _pipeline(U, GOOD, events=_arr(3, 0)) == -1
+    assert "events" in U.last_error()
 
 
 def _merge(U, n=2, o=None, lse=None, b=1, rows=10, heads=2, d=64, out=FAKE, lse_out=None):

@@ -2,16 +2,18 @@
 //
 // Every rule is checked before anything touches the HIP runtime, so a bad
 // call returns its status with nothing enqueued (and can be exercised on a
-// machine without a GPU).  This file allocates nothing and keeps no state
-// except the per-thread text of the last validation failure and the cached
-// compute-unit count per device (the split attention's workspace belongs to
-// the attention launcher).
+// machine without a GPU).  The library allocates nothing: device buffers,
+// the attention workspace and the pipeline's events all belong to the
+// caller.  The only state is the per-thread text of the last validation
+// failure and a cache of each device's compute-unit count (atomic; a value
+// the runtime reports the same way every time).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/ulys.h"
 #include "internal.h"
@@ -169,32 +171,32 @@ SplitChoice auto_split(long long batch, long long q_rows, long long kv_rows, int
   return best;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device.  Threads may race
+// to fill an entry; they store the same value, and atomics make that race
+// well defined.
+constexpr int kCachedDevices = 64;
+std::atomic<int> g_cus[kCachedDevices];
+
 int device_cus(int* cus) {
-  static int cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *cus = cache[dev];
-    return ULYS_OK;
+  const bool cached = dev >= 0 && dev < kCachedDevices;
+  if (cached) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return ULYS_OK;
+    }
   }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_status(e);
   if (n < 1) return fail(ULYS_EHIP, "device reports %d compute units", n);
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (cached) g_cus[dev].store(n, std::memory_order_relaxed);
   *cus = n;
   return ULYS_OK;
 }
-
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
 
 // Validated launch arguments of a pack; nothing is enqueued.
 int prepare_pack(const ulys_layout* L, int rank, int group, const void* const* q_shards,
@@ -302,21 +304,51 @@ int prepare_attend(int batch, int q_rows, int kv_rows, int hq, int hkv, int head
   return ULYS_OK;
 }
 
-// The automatic key-range split (from the device's compute units and the
-// shape) of validated arguments; the first HIP call of an attention call.
-int resolve_splits(ulys::AttnArgs& a) {
+// The split of validated arguments: key_splits as given, or (0) the
+// automatic choice for `cus` compute units.
+void resolve_splits_for(ulys::AttnArgs& a, int cus) {
   if (a.splits < 0) {   // a range split: -splits ranges per (b, head)
     a.ranges = -a.splits;
     a.splits = 1;
-    return ULYS_OK;
+    return;
   }
-  if (a.splits != 0) return ULYS_OK;
-  int cus = 0;
-  const int st = device_cus(&cus);
-  if (st) return st;
+  if (a.splits != 0) return;
   const SplitChoice ch = auto_split(a.batch, a.q_rows, a.kv_rows, cus);
   a.splits = ch.c;
   a.ranges = ch.r;
+}
+
+// The split of validated arguments for the current device (the first HIP call
+// of an attention call, when the split is automatic).
+int resolve_splits(ulys::AttnArgs& a) {
+  int cus = 1;
+  if (a.splits == 0) {
+    const int st = device_cus(&cus);
+    if (st) return st;
+  }
+  resolve_splits_for(a, cus);
+  return ULYS_OK;
+}
+
+// Workspace bytes a resolved call needs for all its heads in one launch
+// (`min_bytes`: for one head per launch; both 0 without a split).
+void workspace_need(const ulys::AttnArgs& a, int head_dim, size_t* all_heads, size_t* min_bytes) {
+  const ulys::WorkspaceSize w = ulys::attn_workspace_size(a, head_dim);
+  *all_heads = w.per_head == 0 ? 0 : w.fixed + w.per_head * (size_t)a.hq;
+  *min_bytes = w.per_head == 0 ? 0 : w.fixed + w.per_head;
+}
+
+// The caller's workspace must hold at least one head's partials of a split
+// call (fewer than all heads: the heads run in several launches).
+int check_workspace(const ulys::AttnArgs& a, int head_dim, const void* ws, size_t ws_bytes) {
+  size_t all = 0, need = 0;
+  workspace_need(a, head_dim, &all, &need);
+  if (need == 0) return ULYS_OK;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(ULYS_EINVAL, "workspace of %zu bytes%s is below the %zu bytes this call needs (%zu for all heads "
+                "in one launch; ulys_attend_workspace_bytes)", ws == nullptr ? (size_t)0 : ws_bytes,
+                ws == nullptr ? " (NULL)" : "", need, all);
+  if ((uintptr_t)ws & 255u) return fail(ULYS_EINVAL, "workspace is not 256-byte aligned");
   return ULYS_OK;
 }
 
@@ -370,23 +402,43 @@ int ulys_amax_bf16(const void* const* tensors, int n_tensors, size_t elems_each,
 
 int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
                       const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
-                      const int32_t* key_gaps, void* o, float* lse, void* stream) {
-  ulys::AttnArgs a;
-  int st = prepare_attend(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax,
-                          key_gaps, nullptr, 0, o, lse, a);
-  if (st || (st = resolve_splits(a))) return st;
-  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
+                      const int32_t* key_gaps, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return ulys_attend_group_ex(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax,
+                              key_gaps, nullptr, 0, o, lse, workspace, workspace_bytes, stream);
 }
 
 int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, int head_dim, const void* q,
                          const void* k, const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
                          const int32_t* key_gaps, const uint32_t* key_mask, int key_splits, void* o, float* lse,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   ulys::AttnArgs a;
   int st = prepare_attend(batch, q_rows, kv_rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale,
                           qk_amax, key_gaps, key_mask, key_splits, o, lse, a);
-  if (st || (st = resolve_splits(a))) return st;
-  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, (hipStream_t)stream));
+  if (st || (st = resolve_splits(a)) || (st = check_workspace(a, head_dim, workspace, workspace_bytes))) return st;
+  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, workspace, workspace_bytes,
+                                      (hipStream_t)stream));
+}
+
+long long ulys_attend_workspace_bytes(int batch, int q_rows, int kv_rows, int heads, int head_dim, int key_splits,
+                                      int compute_units) {
+  if (batch < 1 || q_rows < 1 || kv_rows < 1 || heads < 1 || compute_units < 1)
+    return fail(ULYS_EINVAL, "batch, q_rows, kv_rows, heads and compute_units must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(ULYS_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
+  if (key_splits < -ulys::kMaxRanges || key_splits > ulys::kMaxKeySplits)
+    return fail(ULYS_EINVAL, "key_splits %d outside [%d, %d]", key_splits, -ulys::kMaxRanges, ulys::kMaxKeySplits);
+  ulys::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.batch = batch;
+  a.q_rows = q_rows;
+  a.kv_rows = kv_rows;
+  a.hq = heads;
+  a.splits = key_splits;
+  resolve_splits_for(a, compute_units);
+  size_t all = 0, one = 0;
+  workspace_need(a, head_dim, &all, &one);
+  ok();
+  return (long long)all;
 }
 
 int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, void* const* o_shards, void* stream) {
@@ -399,7 +451,8 @@ int ulys_unpack(const ulys_layout* L, int rank, int group, const void* o_slot, v
 int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shards, const void* const* k_shards,
                        const void* const* v_shards, void* q_slots, void* k_slots, void* v_slots, void* o_slots,
                        float* lse, void* const* o_shards, int qk_dtype, const float* qk_amax, float softmax_scale,
-                       const int32_t* key_gaps, void* stream, void* copy_stream) {
+                       const int32_t* key_gaps, void* const* events, void* workspace, size_t workspace_bytes,
+                       void* stream, void* copy_stream) {
   // Validate everything with group -1 (all groups) before anything is enqueued.
   ulys::PackArgs pk;
   int st = prepare_pack(L, rank, -1, q_shards, k_shards, v_shards, q_slots, k_slots, v_slots, qk_dtype, qk_amax, pk);
@@ -415,29 +468,23 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
     return st;
   if (G > ulys::kMaxPipelineGroups)
     return fail(ULYS_EUNSUPPORTED, "pipeline of %d groups exceeds %d", G, ulys::kMaxPipelineGroups);
-  if ((st = resolve_splits(at))) return st;
+  if (events == nullptr) return fail(ULYS_EINVAL, "events pointer array is NULL");
+  for (int i = 0; i < 3; ++i)
+    if (events[i] == nullptr) return fail(ULYS_EINVAL, "events[%d] is NULL", i);
+  if ((st = resolve_splits(at)) || (st = check_workspace(at, L->head_dim, workspace, workspace_bytes))) return st;
   const bool fp8 = qk_dtype == ULYS_FP8_E4M3;
   const size_t qk_elem = fp8 ? 1 : 2;
   const size_t elems_q = (size_t)L->batch * q_rows * gq * L->head_dim;
   const size_t elems_kv = (size_t)L->batch * kv_rows * gkv * L->head_dim;
   hipStream_t cs = (hipStream_t)stream, xs = (hipStream_t)copy_stream;
 
-  // Events: start (compute -> copy), pack(g) (copy -> compute), attend(g)
-  // (compute -> copy), done (copy -> compute).  Destroying a recorded event
-  // before it completes is deferred by the runtime, so they are released at
-  // the end of the call.
-  hipEvent_t ev[2 * ulys::kMaxPipelineGroups + 2];
-  const int nev = 2 * G + 2;
-  for (int i = 0; i < nev; ++i) {
-    const hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
-      return hip_status(e);
-    }
-  }
-  hipEvent_t ev_start = ev[0], ev_done = ev[1];
-  hipEvent_t* ev_pack = ev + 2;
-  hipEvent_t* ev_att = ev + 2 + G;
+  // The caller's three events.  A stream wait takes the event's state when it
+  // is enqueued, so an event may be recorded again once its wait is enqueued:
+  // ev_sync carries every single hand-over (start, attention g -> unpack g,
+  // done), each waited on right after it is recorded; packs g and g + 1 are
+  // outstanding together, so they alternate between ev_pack[0] and [1].
+  hipEvent_t ev_sync = (hipEvent_t)events[0];
+  hipEvent_t ev_pack[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
 
   auto pack_g = [&](int g) {
     ulys::PackArgs a = pk;
@@ -456,7 +503,7 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
     a.v = (const unsigned char*)v_slots + (size_t)g * elems_kv * 2;
     a.o = (uint16_t*)o_slots + (size_t)g * elems_q;
     a.lse = lse == nullptr ? nullptr : lse + (size_t)g * L->batch * gq * q_rows;
-    return ulys::launch_attn(a, L->head_dim, fp8, cs);
+    return ulys::launch_attn(a, L->head_dim, fp8, workspace, workspace_bytes, cs);
   };
   auto unpack_g = [&](int g) {
     ulys::UnpackArgs a = up;
@@ -469,26 +516,26 @@ int ulys_rank_pipeline(const ulys_layout* L, int rank, const void* const* q_shar
   // copy stream: pack 0, pack 1, [attend 0] unpack 0, pack 2, [attend 1] unpack 1, ...
   // compute stream: [pack g] attend g.  Each group has its own slots, so a
   // pack only has to precede its own attention and an unpack follow it.
-  hipError_t e = hipEventRecord(ev_start, cs);
-  if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_start, 0);
+  // Attention launches share the workspace in compute-stream order.
+  hipError_t e = hipEventRecord(ev_sync, cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_sync, 0);
   for (int g = 0; e == hipSuccess && g < G && g < 2; ++g) {
     e = pack_g(g);
-    if (e == hipSuccess) e = hipEventRecord(ev_pack[g], xs);
+    if (e == hipSuccess) e = hipEventRecord(ev_pack[g & 1], xs);
   }
   for (int g = 0; e == hipSuccess && g < G; ++g) {
-    e = hipStreamWaitEvent(cs, ev_pack[g], 0);
+    e = hipStreamWaitEvent(cs, ev_pack[g & 1], 0);
     if (e == hipSuccess) e = attend_g(g);
-    if (e == hipSuccess) e = hipEventRecord(ev_att[g], cs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_att[g], 0);
+    if (e == hipSuccess) e = hipEventRecord(ev_sync, cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(xs, ev_sync, 0);
     if (e == hipSuccess) e = unpack_g(g);
     if (e == hipSuccess && g + 2 < G) {
       e = pack_g(g + 2);
-      if (e == hipSuccess) e = hipEventRecord(ev_pack[g + 2], xs);
+      if (e == hipSuccess) e = hipEventRecord(ev_pack[g & 1], xs);
     }
   }
-  if (e == hipSuccess) e = hipEventRecord(ev_done, xs);
-  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev_done, 0);
-  for (int i = 0; i < nev; ++i) (void)hipEventDestroy(ev[i]);
+  if (e == hipSuccess) e = hipEventRecord(ev_sync, xs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev_sync, 0);
   return hip_status(e);
 }
 

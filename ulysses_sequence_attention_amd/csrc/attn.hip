@@ -49,8 +49,6 @@
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1005,46 +1003,27 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Split workspace of one (device, stream): calls on one stream run in order,
-// so they may share it; calls on different streams get their own.  Grown on
-// demand, kept until the process ends.
-struct Workspace {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
-
-hipError_t split_workspace(hipStream_t s, size_t bytes, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& w = g_ws[{dev, (uintptr_t)s}];
-  if (w.bytes < bytes) {
-    if (w.ptr != nullptr) {
-      // earlier calls on this stream may still read the old buffer
-      if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-      if ((e = hipFree(w.ptr)) != hipSuccess) return e;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    if ((e = hipMalloc(&w.ptr, bytes)) != hipSuccess) {
-      w.ptr = nullptr;
-      return e;
-    }
-    w.bytes = bytes;
+// Workspace of a split launch: fp32 partial o and lse per head (key-range
+// split: every chunk of every row; range split: two tile pieces per range),
+// then one int per batch (the range split's tile count).
+WorkspaceSize workspace_size(const AttnArgs& a, int D) {
+  WorkspaceSize w{0, 0, 0, 0};
+  if (a.ranges > 0) {
+    w.o_per_head = (size_t)a.batch * a.ranges * 2 * kBM * D * sizeof(float);
+    w.lse_per_head = (size_t)a.batch * a.ranges * 2 * kBM * sizeof(float);
+  } else if (a.splits > 1) {
+    w.o_per_head = (size_t)a.splits * a.batch * a.q_rows * D * sizeof(float);
+    w.lse_per_head = (size_t)a.splits * a.batch * a.q_rows * sizeof(float);
+  } else {
+    return w;
   }
-  *out = w.ptr;
-  return hipSuccess;
+  w.fixed = ((size_t)a.batch * sizeof(int) + 255) & ~(size_t)255;
+  w.per_head = w.o_per_head + w.lse_per_head;
+  return w;
 }
 
-// Largest split workspace one call uses; a call whose heads need more runs
-// as several launches over head ranges (each head's bytes are unchanged).
-constexpr size_t kSplitWorkspaceCap = size_t(2) << 30;
-
 template <int D, bool FP8>
-hipError_t launch(const AttnArgs& in, hipStream_t s) {
+hipError_t launch(const AttnArgs& in, void* ws, size_t ws_bytes, hipStream_t s) {
   AttnArgs a = in;
   a.qtiles = (a.q_rows + kBM - 1) / kBM;
   a.head0 = 0;
@@ -1054,36 +1033,30 @@ hipError_t launch(const AttnArgs& in, hipStream_t s) {
     a.splits = 1;
     return launch_one<D, FP8>(a, s);
   }
-  size_t o_per_head, l_per_head;
-  if (a.ranges > 0) {
-    o_per_head = (size_t)a.batch * a.ranges * 2 * kBM * D * sizeof(float);
-    l_per_head = (size_t)a.batch * a.ranges * 2 * kBM * sizeof(float);
-  } else {
-    o_per_head = (size_t)a.splits * a.batch * a.q_rows * D * sizeof(float);
-    l_per_head = (size_t)a.splits * a.batch * a.q_rows * sizeof(float);
-  }
-  const size_t per_head = o_per_head + l_per_head;
-  const int hsub = (int)std::max<size_t>(1, std::min<size_t>((size_t)a.hq, kSplitWorkspaceCap / per_head));
-  const size_t nseq_bytes = (size_t)a.batch * sizeof(int);
-  void* ws = nullptr;
-  hipError_t e = split_workspace(s, per_head * hsub + nseq_bytes, &ws);
-  if (e != hipSuccess) return e;
-  a.part_o = (float*)ws;
-  a.part_lse = (float*)((char*)ws + o_per_head * hsub);
-  a.range_nseq = (int*)((char*)a.part_lse + l_per_head * hsub);
+  // The caller's workspace holds the partials of hsub heads at a time (the
+  // host checked that it holds at least one head's); a call over more heads
+  // runs as several launches over head ranges (each head's bytes unchanged).
+  const WorkspaceSize w = workspace_size(a, D);
+  const int hsub = (int)std::min<size_t>((size_t)a.hq, (ws_bytes - w.fixed) / w.per_head);
+  a.range_nseq = (int*)ws;
+  a.part_o = (float*)((char*)ws + w.fixed);
+  a.part_lse = (float*)((char*)a.part_o + w.o_per_head * hsub);
   for (int h0 = 0; h0 < a.hq; h0 += hsub) {
     a.head0 = h0;
     a.hsub = std::min(hsub, a.hq - h0);
-    if ((e = launch_one<D, FP8>(a, s)) != hipSuccess) return e;
+    const hipError_t e = launch_one<D, FP8>(a, s);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, hipStream_t s) {
-  if (head_dim == 128) return fp8 ? launch<128, true>(a, s) : launch<128, false>(a, s);
-  return fp8 ? launch<64, true>(a, s) : launch<64, false>(a, s);
+WorkspaceSize attn_workspace_size(const AttnArgs& a, int head_dim) { return workspace_size(a, head_dim); }
+
+hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (head_dim == 128) return fp8 ? launch<128, true>(a, ws, ws_bytes, s) : launch<128, false>(a, ws, ws_bytes, s);
+  return fp8 ? launch<64, true>(a, ws, ws_bytes, s) : launch<64, false>(a, ws, ws_bytes, s);
 }
 
 }  // namespace ulys

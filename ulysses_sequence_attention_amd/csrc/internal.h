@@ -97,7 +97,17 @@ struct AttnArgs {
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);
 hipError_t launch_amax(const AmaxArgs& a, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, hipStream_t s);
+// Device workspace of a split attention launch (zero per_head: no split).
+// A call needs fixed + per_head * heads bytes to run all heads in one launch,
+// and at least fixed + per_head (one head per launch).
+struct WorkspaceSize {
+  size_t per_head;       // partial o + lse of one head
+  size_t o_per_head;
+  size_t lse_per_head;
+  size_t fixed;          // the range split's per-batch tile counts (256-byte padded)
+};
+WorkspaceSize attn_workspace_size(const AttnArgs& a, int head_dim);   // a: splits/ranges resolved
+hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace ulys

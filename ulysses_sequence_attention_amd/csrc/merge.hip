@@ -1,8 +1,8 @@
 // Merge of partial attention results over key blocks by their log-sum-exp
-// (flashdreams cp.py, ContextParallelAttention._impl_ring: each step's
-// (out, lse) is absorbed with weights sigmoid(lse - prev_lse), and the LSE
-// grows by -logsigmoid(prev_lse - lse)).  Absorbing n blocks one after the
-// other is, in exact arithmetic, one weighted sum:
+// (flashdreams cp.py, ContextParallelAttention, ring path: the running result
+// takes in each block's output with a logistic weight of the LSE difference,
+// and its LSE becomes the log of the summed exponentials).  Taking in n
+// blocks one after the other is, in exact arithmetic, one weighted sum:
 //   L = log sum_i exp(lse_i),  out = sum_i exp(lse_i - L) out_i,
 // which this kernel evaluates in fp32 in one pass (max-shifted, so no
 // overflow; a block with lse = -inf has weight 0).

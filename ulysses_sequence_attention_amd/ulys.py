@@ -41,11 +41,14 @@ _lib.ulys_pack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, ctypes.POINTER(_
 _lib.ulys_pack.restype = _i
 _lib.ulys_amax_bf16.argtypes = [ctypes.POINTER(_vp), _i, ctypes.c_size_t, _vp, _vp]
 _lib.ulys_amax_bf16.restype = _i
+_sz = ctypes.c_size_t
 _lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
-                                   ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
+                                   ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp, _sz, _vp]
 _lib.ulys_attend_group.restype = _i
 _lib.ulys_attend_group_ex.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
-                                      ctypes.POINTER(ctypes.c_int32), _vp, _i, _vp, _vp, _vp]
+                                      ctypes.POINTER(ctypes.c_int32), _vp, _i, _vp, _vp, _vp, _sz, _vp]
+_lib.ulys_attend_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.ulys_attend_workspace_bytes.restype = ctypes.c_longlong
 _lib.ulys_attend_group_ex.restype = _i
 _lib.ulys_attend_splits.argtypes = [_i, _i, _i, _i]
 _lib.ulys_attend_splits.restype = _i
@@ -55,7 +58,7 @@ _lib.ulys_unpack.argtypes = [ctypes.POINTER(ulys_layout), _i, _i, _vp, ctypes.PO
 _lib.ulys_unpack.restype = _i
 _lib.ulys_rank_pipeline.argtypes = [ctypes.POINTER(ulys_layout), _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                     ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _i, _vp,
-                                    ctypes.c_float, _vp, _vp, _vp]
+                                    ctypes.c_float, _vp, ctypes.POINTER(_vp), _vp, _sz, _vp, _vp]
 _lib.ulys_rank_pipeline.restype = _i
 _lib.ulys_lse_merge.argtypes = [_i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.ulys_lse_merge.restype = _i
@@ -67,7 +70,7 @@ _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits",
-            "ulys_attend_ranges",
+            "ulys_attend_ranges", "ulys_attend_workspace_bytes",
             "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror",
             "ulys_last_error")
 
@@ -157,6 +160,36 @@ def _ptrs(ts, name, dtypes, numel):
     return arr
 
 
+def _cus(device) -> int:
+    return torch.cuda.get_device_properties(device).multi_processor_count
+
+
+def ulys_attend_workspace_bytes(batch: int, q_rows: int, kv_rows: int, heads: int, head_dim: int,
+                                key_splits: int = 0, compute_units: int | None = None) -> int:
+    """Workspace bytes an attention call of this shape needs for all ``heads`` in one launch (0: no split).
+
+    ``compute_units`` defaults to the current device's count (the automatic split depends on it)."""
+    cus = _cus(torch.cuda.current_device()) if compute_units is None else int(compute_units)
+    n = _lib.ulys_attend_workspace_bytes(int(batch), int(q_rows), int(kv_rows), int(heads), int(head_dim),
+                                         int(key_splits), cus)
+    _check(int(min(n, 0)))
+    return int(n)
+
+
+def _workspace(workspace, device, batch, q_rows, kv_rows, heads, head_dim, key_splits, stream):
+    """(pointer, bytes) of the caller's workspace, or of a new torch buffer sized for the call (kept alive by
+    torch's allocator until the work on ``stream`` that uses it is done)."""
+    if workspace is None:
+        n = ulys_attend_workspace_bytes(batch, q_rows, kv_rows, heads, head_dim, key_splits, _cus(device))
+        if n == 0:
+            return None, 0, None
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        workspace.record_stream(torch.cuda.current_stream(device) if stream is None else stream)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
 _BF16 = (torch.bfloat16,)
 _QK8 = (torch.uint8, torch.float8_e4m3fn)
 
@@ -195,10 +228,12 @@ def ulys_amax_bf16(tensors, out: torch.Tensor, stream=None) -> None:
 def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       lse: torch.Tensor | None = None, softmax_scale: float = 0.0,
                       key_gaps=None, qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None,
-                      stream=None) -> None:
+                      workspace: torch.Tensor | None = None, stream=None) -> None:
     """Attention on one slot: q ``[B, rows, hq, D]``, k/v ``[B, rows, hkv, D]`` -> o (and lse ``[B, hq, rows]``).
 
-    ``key_gaps``: per-batch ``(start, end)`` masked key ranges, or None.
+    ``key_gaps``: per-batch ``(start, end)`` masked key ranges, or None.  ``workspace``: a GPU byte buffer of at
+    least the size :func:`ulys_attend_workspace_bytes` gives for one head (None: a torch buffer of the full size
+    is allocated for the call).
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
@@ -218,14 +253,16 @@ def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
         if len(key_gaps) != b:
             raise ValueError("key_gaps needs one (start, end) per batch")
         gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
+    wp, wn, _keep = _workspace(workspace, q.device, b, rows, rows, hq, d, 0, stream)
     _check(_lib.ulys_attend_group(b, rows, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, op, lp,
-                                  _stream(stream)))
+                                  wp, wn, _stream(stream)))
 
 
 def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                          lse: torch.Tensor | None = None, softmax_scale: float = 0.0, key_gaps=None,
                          key_mask: torch.Tensor | None = None, qk_dtype: int = ULYS_BF16,
-                         qk_amax: torch.Tensor | None = None, key_splits: int = 0, stream=None) -> None:
+                         qk_amax: torch.Tensor | None = None, key_splits: int = 0,
+                         workspace: torch.Tensor | None = None, stream=None) -> None:
     """Attention with q ``[B, Nq, hq, D]`` and k/v ``[B, Nk, hkv, D]`` (Nq may differ from Nk) -> o ``[B, Nq, hq, D]``
     (and lse ``[B, hq, Nq]``).
 
@@ -233,6 +270,7 @@ def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
     valid key ``j``, or None (all keys valid).  ``key_gaps`` as for :func:`ulys_attend_group`.
     ``key_splits``: 0 = automatic (:func:`ulys_attend_splits`, else :func:`ulys_attend_ranges`), 1 = none,
     2..16 = that many key-range runs per query tile, ``-R`` = a range split into R runs per (b, head).
+    ``workspace`` as for :func:`ulys_attend_group` (sized with the same ``key_splits``).
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
@@ -255,8 +293,9 @@ def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
         if len(key_gaps) != b:
             raise ValueError("key_gaps needs one (start, end) per batch")
         gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
+    wp, wn, _keep = _workspace(workspace, q.device, b, nq, nk, hq, d, key_splits, stream)
     _check(_lib.ulys_attend_group_ex(b, nq, nk, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, mp,
-                                     int(key_splits), op, lp, _stream(stream)))
+                                     int(key_splits), op, lp, wp, wn, _stream(stream)))
 
 
 def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_shards, stream=None) -> None:
@@ -274,11 +313,13 @@ def ulys_unpack(layout: Layout, rank: int, group: int, o_slot: torch.Tensor, o_s
 def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, q_slots, k_slots, v_slots,
                        o_slots, o_shards, lse: torch.Tensor | None = None, softmax_scale: float = 0.0,
                        key_gaps=None, qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None,
-                       stream=None, copy_stream=None) -> None:
+                       events=None, workspace: torch.Tensor | None = None, stream=None, copy_stream=None) -> None:
     """Pack, attend and unpack every head group of ``rank``; repack on ``copy_stream`` overlaps attention.
 
     Slots hold all G groups (``[G, B, rows, Gh, D]``; q/o with ``rows_q`` rows), lse ``[G, B, Gq, rows_q]`` or None.
-    ``copy_stream`` None means the same stream as ``stream`` (sequential).
+    ``copy_stream`` None means the same stream as ``stream`` (sequential).  ``events``: three
+    ``torch.cuda.Event`` objects the library records and waits on (reusable across calls; None: three new
+    ones).  ``workspace`` as for :func:`ulys_attend_group`, for one group's attention.
     """
     L = layout
     if len(q_shards) != L.degree or len(k_shards) != L.degree or len(v_shards) != L.degree:
@@ -306,9 +347,19 @@ def ulys_rank_pipeline(layout: Layout, rank: int, q_shards, k_shards, v_shards, 
         gaps = (ctypes.c_int32 * (2 * L.batch))(*[int(x) for g in key_gaps for x in g])
     s = _stream(stream)
     x = s if copy_stream is None else _stream(copy_stream)
+    if events is None:
+        events = [torch.cuda.Event() for _ in range(3)]
+    if len(events) != 3:
+        raise ValueError("need three events")
+    ev = (_vp * 3)()
+    for i, e in enumerate(events):
+        if e.cuda_event == 0:            # torch creates the HIP event on its first record
+            e.record(torch.cuda.current_stream() if stream is None else stream)
+        ev[i] = e.cuda_event
+    wp, wn, _keep = _workspace(workspace, q_slots.device, L.batch, L.rows_q, L.rows, L.gq, L.head_dim, 0, stream)
     c = L.c_struct()
     _check(_lib.ulys_rank_pipeline(ctypes.byref(c), rank, qa, ka, va, qs, ks, vs, os_, lp, oa, qk_dtype, am,
-                                   float(softmax_scale), gaps, s, x))
+                                   float(softmax_scale), gaps, ev, wp, wn, s, x))
 
 
 def ulys_lse_merge(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tensor | None = None,
