@@ -12,7 +12,8 @@
  * (per-tensor fp8 scale source), ulys_attend_group_ex (different query and key
  * lengths, key masks, an explicit work split), ulys_attend_splits /
  * ulys_attend_ranges / ulys_auto_groups / ulys_attend_workspace_bytes (the
- * automatic choices and the workspace size, host-only), ulys_strerror and
+ * automatic choices and the workspace size, host-only), ulys_attend_group_noalloc
+ * (attention for callers that cannot allocate), ulys_strerror and
  * ulys_last_error.
  *
  * Conventions shared by every call
@@ -26,8 +27,9 @@
  *     between calls.  Scratch memory (the attention workspace) and the
  *     pipeline's events are the caller's, passed in like the tensors
  *     (sglang PR #43521, "Buffers": the caller's pool holds every buffer of
- *     the path).  The only state is the text behind ulys_last_error and a
- *     cache of each device's compute-unit count.
+ *     the path).  The only state is the text behind ulys_last_error, a
+ *     cache of each device's compute-unit count, and the static scratch
+ *     array of ulys_attend_group_noalloc (with its per-device address).
  *   - All validation happens before anything is enqueued.  On failure the
  *     call returns a negative ulys_status, enqueues nothing, and
  *     ulys_last_error() describes the first violated rule.
@@ -278,6 +280,26 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
                       float softmax_scale, const float* qk_amax,
                       const int32_t* key_gaps, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ulys_attend_group_noalloc -- ulys_attend_group for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and the same bytes.
+ *
+ * The split partials live in a static device array of the library, 128 MiB
+ * per GPU, held from the first call on that GPU until the process ends; the call itself allocates nothing.  A call whose heads
+ * need more than the array runs them in several launches (as a small
+ * workspace does for ulys_attend_group); one whose single head needs more is
+ * ULYS_EINVAL with nothing enqueued.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, no ordering
+ * between them) race and may return wrong results; calls ordered on one
+ * stream are safe.  Nothing in the array has to start at zero.
+ */
+int ulys_attend_group_noalloc(int batch, int rows, int hq, int hkv, int head_dim,
+                              const void* q, const void* k, const void* v, int qk_dtype,
+                              float softmax_scale, const float* qk_amax,
+                              const int32_t* key_gaps, void* o, float* lse, void* stream);
 
 /*
  * ulys_attend_group_ex -- ulys_attend_group with query and key sequences of

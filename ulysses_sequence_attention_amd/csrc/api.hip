@@ -420,6 +420,27 @@ int ulys_attend_group_ex(int batch, int q_rows, int kv_rows, int hq, int hkv, in
                                       (hipStream_t)stream));
 }
 
+int ulys_attend_group_noalloc(int batch, int rows, int hq, int hkv, int head_dim, const void* q, const void* k,
+                              const void* v, int qk_dtype, float softmax_scale, const float* qk_amax,
+                              const int32_t* key_gaps, void* o, float* lse, void* stream) {
+  ulys::AttnArgs a;
+  int st = prepare_attend(batch, rows, rows, hq, hkv, head_dim, q, k, v, qk_dtype, softmax_scale, qk_amax, key_gaps,
+                          nullptr, 0, o, lse, a);
+  if (st || (st = resolve_splits(a))) return st;
+  size_t all = 0, need = 0;
+  workspace_need(a, head_dim, &all, &need);
+  if (need > ulys::kScratchBytes)
+    return fail(ULYS_EINVAL, "one head of this call needs %zu bytes of scratch, above the library's static %zu "
+                "(use ulys_attend_group with a workspace)", need, ulys::kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = ulys::scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(ulys::launch_attn(a, head_dim, qk_dtype == ULYS_FP8_E4M3, ws, need > 0 ? ulys::kScratchBytes : 0,
+                                      (hipStream_t)stream));
+}
+
 long long ulys_attend_workspace_bytes(int batch, int q_rows, int kv_rows, int heads, int head_dim, int key_splits,
                                       int compute_units) {
   if (batch < 1 || q_rows < 1 || kv_rows < 1 || heads < 1 || compute_units < 1)

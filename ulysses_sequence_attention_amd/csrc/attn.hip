@@ -49,6 +49,7 @@
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1057,6 +1058,39 @@ WorkspaceSize attn_workspace_size(const AttnArgs& a, int head_dim) { return work
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, void* ws, size_t ws_bytes, hipStream_t s) {
   if (head_dim == 128) return fp8 ? launch<128, true>(a, ws, ws_bytes, s) : launch<128, false>(a, ws, ws_bytes, s);
   return fp8 ? launch<64, true>(a, ws, ws_bytes, s) : launch<64, false>(a, ws, ws_bytes, s);
+}
+
+// ---- static scratch for callers that cannot allocate ----
+// The workspace of ulys_attend_group_noalloc: one array per GPU, alive until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array: kernels get the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device and cached.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kScratchDevices;
+  if (cached) {
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p != nullptr) {
+      *out = p;
+      return hipSuccess;
+    }
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  if (cached) g_scratch[dev].store(p, std::memory_order_release);   // every thread finds the same address
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace ulys

@@ -110,4 +110,10 @@ WorkspaceSize attn_workspace_size(const AttnArgs& a, int head_dim);   // a: spli
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool fp8, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 
+// Static scratch of ulys_attend_group_noalloc: kScratchBytes per GPU, held by
+// the library from the first use on that GPU until the process ends.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+// Device address of the current GPU's scratch (resolved once per device).
+hipError_t scratch_address(void** out);
+
 }  // namespace ulys

@@ -47,6 +47,9 @@ _lib.ulys_attend_group.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes
 _lib.ulys_attend_group.restype = _i
 _lib.ulys_attend_group_ex.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
                                       ctypes.POINTER(ctypes.c_int32), _vp, _i, _vp, _vp, _vp, _sz, _vp]
+_lib.ulys_attend_group_noalloc.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _i, ctypes.c_float, _vp,
+                                           ctypes.POINTER(ctypes.c_int32), _vp, _vp, _vp]
+_lib.ulys_attend_group_noalloc.restype = _i
 _lib.ulys_attend_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.ulys_attend_workspace_bytes.restype = ctypes.c_longlong
 _lib.ulys_attend_group_ex.restype = _i
@@ -70,7 +73,7 @@ _lib.ulys_last_error.argtypes = []
 _lib.ulys_last_error.restype = ctypes.c_char_p
 
 EXPORTED = ("ulys_pack", "ulys_amax_bf16", "ulys_attend_group", "ulys_attend_group_ex", "ulys_attend_splits",
-            "ulys_attend_ranges", "ulys_attend_workspace_bytes",
+            "ulys_attend_ranges", "ulys_attend_workspace_bytes", "ulys_attend_group_noalloc",
             "ulys_unpack", "ulys_rank_pipeline", "ulys_lse_merge", "ulys_auto_groups", "ulys_strerror",
             "ulys_last_error")
 
@@ -256,6 +259,33 @@ def ulys_attend_group(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     wp, wn, _keep = _workspace(workspace, q.device, b, rows, rows, hq, d, 0, stream)
     _check(_lib.ulys_attend_group(b, rows, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps, op, lp,
                                   wp, wn, _stream(stream)))
+
+
+def ulys_attend_group_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                              lse: torch.Tensor | None = None, softmax_scale: float = 0.0, key_gaps=None,
+                              qk_dtype: int = ULYS_BF16, qk_amax: torch.Tensor | None = None, stream=None) -> None:
+    """:func:`ulys_attend_group` without a workspace: the library's static per-GPU scratch holds the split
+    partials (no allocation anywhere in the call).  Calls that overlap on one GPU race on that scratch."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D [B, rows, heads, D]")
+    b, rows, hq, d = q.shape
+    hkv = k.shape[2]
+    if tuple(k.shape) != (b, rows, hkv, d) or tuple(v.shape) != (b, rows, hkv, d) or tuple(o.shape) != (b, rows, hq, d):
+        raise ValueError("shape mismatch between q, k, v and o")
+    qk_t = _QK8 if qk_dtype == ULYS_FP8_E4M3 else _BF16
+    qp = _dev(q, "q", qk_t)
+    kp = _dev(k, "k", qk_t)
+    vp = _dev(v, "v", _BF16)
+    op = _dev(o, "o", _BF16)
+    lp = None if lse is None else _dev(lse, "lse", (torch.float32,), b * hq * rows)
+    am = None if qk_amax is None else _dev(qk_amax, "qk_amax", (torch.float32,), 2)
+    gaps = None
+    if key_gaps is not None:
+        if len(key_gaps) != b:
+            raise ValueError("key_gaps needs one (start, end) per batch")
+        gaps = (ctypes.c_int32 * (2 * b))(*[int(x) for g in key_gaps for x in g])
+    _check(_lib.ulys_attend_group_noalloc(b, rows, hq, hkv, d, qp, kp, vp, qk_dtype, float(softmax_scale), am, gaps,
+                                          op, lp, _stream(stream)))
 
 
 def ulys_attend_group_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
