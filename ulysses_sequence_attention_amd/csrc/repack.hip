@@ -18,29 +18,21 @@ namespace ulys {
 namespace {
 
 constexpr int kThreads = 256;
-// Access forms and chunks per thread, chosen by measurement on MI355X (Wan
-// Ulysses-4 shapes): pack reads nontemporal and writes plainly, two chunks
-// per thread; unpack reads and writes nontemporal, two chunks per thread.
-#ifndef ULYS_PK_NTLOAD
-#define ULYS_PK_NTLOAD 1
-#endif
-#ifndef ULYS_PK_NTSTORE
-#define ULYS_PK_NTSTORE 0
-#endif
-#ifndef ULYS_UP_NTLOAD
-#define ULYS_UP_NTLOAD 1
-#endif
-#ifndef ULYS_UP_NTSTORE
-#define ULYS_UP_NTSTORE 1
-#endif
-#ifndef ULYS_PK_UNROLL
-#define ULYS_PK_UNROLL 2
-#endif
-#ifndef ULYS_UP_UNROLL
-#define ULYS_UP_UNROLL 2
-#endif
-constexpr int kPackUnroll = ULYS_PK_UNROLL;     // chunks per pack thread
-constexpr int kUnpackUnroll = ULYS_UP_UNROLL;   // chunks per unpack thread
+// Chunks (16 bytes) per thread, chunk order and access forms, chosen by
+// sweeping them on MI355X at the Wan Ulysses-4 rank shapes with two rotating
+// slot sets (nothing cache-resident):
+//  * pack, bf16 tensors: two chunks per thread, the chunks of one slot in
+//    order (contiguous writes), nontemporal loads and stores;
+//  * pack, e4m3 tensors: two chunks per thread, a joint row's chunks group
+//    after group (contiguous reads), nontemporal loads, plain stores;
+//  * unpack: one chunk per thread, a shard row's chunks group after group
+//    (contiguous writes), nontemporal loads, plain stores (+10% over
+//    nontemporal stores);
+//  * amax: eight chunks per thread in flight, 1024 workgroups in all.
+constexpr int kPackUnroll = 2;
+constexpr int kUnpackUnroll = 1;
+constexpr int kAmaxUnroll = 8;
+constexpr int kAmaxBlocks = 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -88,73 +80,90 @@ __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
   else *(u32x4*)p = v;
 }
 
-// grid.x: 16-byte output chunks of one slot [B * rows * cpr], kPackUnroll * kThreads
-// per block, thread i taking chunks i, i + kThreads, ...; grid.y = tensor * ngroups
-// + group.  All loads of a thread are issued before its stores.  Chunk indices
-// are 32-bit (the host rejects slots of 2^32 chunks or more).
+// grid.x: 16-byte output chunks of one tensor's slots [ngroups][B * rows * cpr], kPackUnroll * kThreads
+// per block, thread i taking chunks i, i + kThreads, ...; grid.y = tensor.  bf16 tensors take the chunks
+// slot after slot (consecutive lanes write one contiguous run of a slot); e4m3 tensors take a joint row's
+// chunks group after group (consecutive lanes read one contiguous run of the source row, the launch's
+// heads).  All loads of a thread are issued before its stores.  Chunk indices are 32-bit (the host
+// rejects slots of 2^32 chunks or more).
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
-  const int tensor = blockIdx.y / a.g[0].ngroups;
+  const int tensor = blockIdx.y;
   const RepackGeom& g = a.g[tensor];
-  const int gi = blockIdx.y % g.ngroups;
   const int gh = a.gh[tensor];
   const int D = g.head_dim;
   const int fp8 = a.fp8[tensor];
   const int elems_per_chunk = fp8 ? 16 : 8;       // output chunk is always 16 bytes
-  const unsigned cpr = (unsigned)(gh * D / elems_per_chunk);   // chunks per slot row
-  const unsigned total = (unsigned)g.batch * (unsigned)g.rows * cpr;
+  const unsigned cpr = (unsigned)(gh * D / elems_per_chunk);   // chunks per slot row of one group
+  const unsigned cpr_all = cpr * (unsigned)g.ngroups;          // chunks per joint row, all groups
+  const unsigned per_slot = (unsigned)g.batch * (unsigned)g.rows * cpr;
+  const unsigned total = per_slot * (unsigned)g.ngroups;
   const int H = a.heads[tensor];
-  const int hbase = a.h0[tensor] + gi * gh;
+  const int hbase = a.h0[tensor];
   float inv = 1.0f;
   if (fp8) {
     const float am = a.amax[tensor];
     inv = am > 0.0f ? __fdiv_rn(448.0f, am) : 1.0f;
   }
-  unsigned char* dst_base = (unsigned char*)a.dst[tensor] +
-                            (size_t)gi * g.batch * g.rows * gh * D * (fp8 ? 1 : 2);
   const unsigned first = blockIdx.x * (kPackUnroll * kThreads) + threadIdx.x;
   u32x4 x0[kPackUnroll], x1[kPackUnroll];
+  unsigned ochunk[kPackUnroll];   // output chunk over all slots (gi * per_slot + row chunk)
 #pragma unroll
   for (int u = 0; u < kPackUnroll; ++u) {
     const unsigned idx = first + u * kThreads;
+    ochunk[u] = total;
     if (idx < total) {
-      const unsigned c = idx % cpr;
-      const unsigned bt = idx / cpr;
+      unsigned gi, c, bt;
+      if (fp8) {
+        const unsigned ca = idx % cpr_all;
+        bt = idx / cpr_all;
+        gi = ca / cpr;
+        c = ca - gi * cpr;
+      } else {
+        gi = idx / per_slot;
+        const unsigned rem = idx - gi * per_slot;
+        c = rem % cpr;
+        bt = rem / cpr;
+      }
       const unsigned t = bt % (unsigned)g.rows;
       const unsigned b = bt / (unsigned)g.rows;
       int p, srow;
       src_of_row(g, g.rank, (int)t, &p, &srow);
-      const uint16_t* src = a.src[tensor][p] +
-                            (((size_t)b * g.shard_rows + srow) * H + hbase) * D + (size_t)c * elems_per_chunk;
-      x0[u] = ld_stream<ULYS_PK_NTLOAD>(src);
-      if (fp8) x1[u] = ld_stream<ULYS_PK_NTLOAD>(src + 8);
+      const uint16_t* src = a.src[tensor][p] + (((size_t)b * g.shard_rows + srow) * H + hbase) * D +
+                            (size_t)(gi * cpr + c) * elems_per_chunk;
+      x0[u] = ld_stream<true>(src);
+      if (fp8) x1[u] = ld_stream<true>(src + 8);
+      ochunk[u] = gi * per_slot + bt * cpr + c;
     }
   }
+  unsigned char* dst = (unsigned char*)a.dst[tensor];
 #pragma unroll
   for (int u = 0; u < kPackUnroll; ++u) {
-    const unsigned idx = first + u * kThreads;
-    if (idx < total) {
-      u32x4 y = x0[u];
+    if (ochunk[u] < total) {
       if (fp8) {
+        u32x4 y;
         y.x = e4m3_of_bf16x4(x0[u].x, x0[u].y, inv);
         y.y = e4m3_of_bf16x4(x0[u].z, x0[u].w, inv);
         y.z = e4m3_of_bf16x4(x1[u].x, x1[u].y, inv);
         y.w = e4m3_of_bf16x4(x1[u].z, x1[u].w, inv);
+        st_stream<false>(dst + (size_t)ochunk[u] * 16, y);
+      } else {
+        st_stream<true>(dst + (size_t)ochunk[u] * 16, x0[u]);
       }
-      st_stream<ULYS_PK_NTSTORE>(dst_base + (size_t)idx * 16, y);
     }
   }
 }
 
-// grid.x: chunks of [B * shard_rows * cpr] (as pack); grid.y = p * ngroups + group
+// grid.x: chunks of one output shard's rows [B * shard_rows * ngroups * cpr] (as pack, the launch's heads
+// of a row taken group after group, so consecutive lanes write one contiguous run of the shard row);
+// grid.y = shard p.
 __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a) {
   const RepackGeom& g = a.g;
-  const int p = blockIdx.y / g.ngroups;
-  const int gi = blockIdx.y % g.ngroups;
+  const int p = blockIdx.y;
   const int D = g.head_dim;
   const unsigned cpr = (unsigned)(a.gh * D / 8);
-  const unsigned total = (unsigned)g.batch * (unsigned)g.shard_rows * cpr;
-  const int hbase = a.h0 + gi * a.gh;
-  const uint16_t* src_base = a.src + (size_t)gi * g.batch * g.rows * a.gh * D;
+  const unsigned cpr_all = cpr * (unsigned)g.ngroups;
+  const unsigned total = (unsigned)g.batch * (unsigned)g.shard_rows * cpr_all;
+  const size_t slot_elems = (size_t)g.batch * g.rows * a.gh * D;
   const unsigned first = blockIdx.x * (kUnpackUnroll * kThreads) + threadIdx.x;
   u32x4 x[kUnpackUnroll];
   uint16_t* dst[kUnpackUnroll];
@@ -163,37 +172,48 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a) {
     const unsigned idx = first + u * kThreads;
     dst[u] = nullptr;
     if (idx < total) {
-      const unsigned c = idx % cpr;
-      const unsigned br = idx / cpr;
+      const unsigned ca = idx % cpr_all;
+      const unsigned br = idx / cpr_all;
       const int r = (int)(br % (unsigned)g.shard_rows);      // row within shard p
       const unsigned b = br / (unsigned)g.shard_rows;
+      const unsigned gi = ca / cpr, c = ca - gi * cpr;
       int t;
       if (g.rep_first) t = (r < g.n_rep) ? r : g.n_rep + p * g.s_local + (r - g.n_rep);
       else t = (r < g.s_local) ? p * g.s_local + r : g.degree * g.s_local + (r - g.s_local);
-      x[u] = ld_stream<ULYS_UP_NTLOAD>(src_base + (((size_t)b * g.rows + t) * a.gh) * D + (size_t)c * 8);
-      dst[u] = a.dst[p] + (((size_t)b * g.shard_rows + r) * a.heads + hbase) * D + (size_t)c * 8;
+      x[u] = ld_stream<true>(a.src + gi * slot_elems + (((size_t)b * g.rows + t) * a.gh) * D + (size_t)c * 8);
+      dst[u] = a.dst[p] + (((size_t)b * g.shard_rows + r) * a.heads + a.h0) * D + (size_t)ca * 8;
     }
   }
 #pragma unroll
   for (int u = 0; u < kUnpackUnroll; ++u)
-    if (first + u * kThreads < total) st_stream<ULYS_UP_NTSTORE>(dst[u], x[u]);
+    if (dst[u] != nullptr) st_stream<false>(dst[u], x[u]);
 }
 
 __global__ void amax_zero_kernel(unsigned int* out) {
   if (threadIdx.x == 0) *out = 0u;
 }
 
+// |bf16| maximum of 8 elements as their 15 magnitude bits (finite inputs)
+__device__ __forceinline__ unsigned int max_mag(u32x4 x, unsigned int m) {
+  m = max(m, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu), max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
+  return max(m, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu), max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
+}
+
+// grid: (blocks per tensor, tensors).  Each thread keeps kAmaxUnroll 16-byte loads in flight per round.
 __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
+  const u32x4* src = (const u32x4*)a.src[blockIdx.y];
+  const size_t n = a.chunks_each;
+  const size_t per_round = (size_t)gridDim.x * kThreads * kAmaxUnroll;
   unsigned int m = 0;
-  const size_t total = (size_t)a.n * a.chunks_each;
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
-    const int tsr = (int)(idx / a.chunks_each);
-    const size_t c = idx % a.chunks_each;
-    const u32x4 x = ((const u32x4*)a.src[tsr])[c];
-    // |bf16| ordered as its 15 magnitude bits (finite inputs)
-    m = max(m, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu), max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
-    m = max(m, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu), max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
+  for (size_t base = (size_t)blockIdx.x * kThreads * kAmaxUnroll + threadIdx.x; base < n; base += per_round) {
+    u32x4 x[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      x[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = max_mag(x[u], m);
   }
   for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned int)__shfl_xor((int)m, off, 64));
   __shared__ unsigned int red[kThreads / 64];
@@ -213,19 +233,19 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   long most = 0;
   for (int t = 0; t < 3; ++t) {
     const long cpr = (long)a.gh[t] * a.g[t].head_dim / (a.fp8[t] ? 16 : 8);
-    const long total = (long)a.g[t].batch * a.g[t].rows * cpr;
+    const long total = (long)a.g[t].batch * a.g[t].rows * cpr * a.g[t].ngroups;
     if (total > most) most = total;
   }
   const long per_block = (long)kThreads * kPackUnroll;
-  dim3 grid((unsigned)((most + per_block - 1) / per_block), 3 * a.g[0].ngroups);
+  dim3 grid((unsigned)((most + per_block - 1) / per_block), 3);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s) {
-  const long total = (long)a.g.batch * a.g.shard_rows * (a.gh * a.g.head_dim / 8);
+  const long total = (long)a.g.batch * a.g.shard_rows * (a.gh * a.g.head_dim / 8) * a.g.ngroups;
   const long per_block = (long)kThreads * kUnpackUnroll;
-  dim3 grid((unsigned)((total + per_block - 1) / per_block), a.g.degree * a.g.ngroups);
+  dim3 grid((unsigned)((total + per_block - 1) / per_block), a.g.degree);
   hipLaunchKernelGGL(unpack_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -234,11 +254,13 @@ hipError_t launch_amax(const AmaxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(amax_zero_kernel, dim3(1), dim3(64), 0, s, a.out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t total = (size_t)a.n * a.chunks_each;
-  size_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 2048) blocks = 2048;
+  // about kAmaxBlocks workgroups over all tensors, each keeping 8 chunks per thread in flight
+  const size_t per_block = (size_t)kThreads * kAmaxUnroll;
+  size_t blocks = (a.chunks_each + per_block - 1) / per_block;
+  const size_t cap = (size_t)(kAmaxBlocks + a.n - 1) / a.n;
+  if (blocks > cap) blocks = cap;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks, a.n), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
