@@ -236,6 +236,52 @@ def run_config(torch, ulys, args, stream, L, shards, flops_step, peak, kernel, g
 
 # ---------------------------------------------------------------------------------------------- side figures
 
+def repack_back_to_back(torch, ulys, L, shards, reps: int) -> dict:
+    """Kernel throughput of the repack without per-launch events: `reps` launches of each of pack (bf16 and
+    e4m3 q/k), unpack and amax back to back between two events, ranks cycled and two slot sets rotated
+    (nothing cache-resident).  GB/s of algorithmic bytes (read + write)."""
+    dev = shards["q"][0].device
+    G, P, D, rows = L.groups, L.degree, L.head_dim, L.rows
+    heads = L.hq // P
+    out = {}
+    amax = torch.zeros(2, dtype=torch.float32, device=dev)
+    ulys.ulys_amax_bf16(shards["q"], amax[0:1])
+    ulys.ulys_amax_bf16(shards["k"], amax[1:2])
+
+    def timed(fn, nbytes):
+        for j in range(3):
+            fn(j)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for j in range(reps):
+            fn(j)
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    for fp8 in (False, True):
+        qk = torch.uint8 if fp8 else torch.bfloat16
+        sets = [[torch.empty((G, 1, rows, L.gq, D), dtype=qk, device=dev) for _ in range(2)] +
+                [torch.empty((G, 1, rows, L.gkv, D), dtype=torch.bfloat16, device=dev)] for _ in range(2)]
+        nbytes = rows * heads * D * (3 * 2 + 2 * (1 if fp8 else 2) + 2)
+        out["fp8_pack_gbs" if fp8 else "pack_gbs"] = timed(
+            lambda j: ulys.ulys_pack(L, j % P, -1, shards["q"], shards["k"], shards["v"], *sets[j % 2],
+                                     qk_dtype=ulys.ULYS_FP8_E4M3 if fp8 else ulys.ULYS_BF16,
+                                     qk_amax=amax if fp8 else None), nbytes)
+        del sets
+    oslots = [torch.empty((G, 1, rows, L.gq, D), dtype=torch.bfloat16, device=dev).normal_() for _ in range(2)]
+    o_shards = [torch.empty_like(x) for x in shards["q"]]
+    out["unpack_gbs"] = timed(lambda j: ulys.ulys_unpack(L, j % P, -1, oslots[j % 2], o_shards), 2 * rows * heads * D * 2)
+    n_amax = sum(x.numel() * 2 for x in shards["q"])
+    out["amax_gbs"] = timed(lambda j: ulys.ulys_amax_bf16(shards["q" if j % 2 == 0 else "k"], amax[j % 2:j % 2 + 1]),
+                            n_amax)
+    for k_ in ("pack_gbs", "fp8_pack_gbs", "unpack_gbs", "amax_gbs"):
+        out[k_.replace("_gbs", "_frac_hbm_peak")] = round(out[k_] / PEAK_HBM_GBS, 4)
+    out["launches_each"] = reps
+    return out
+
+
 def merge_gbs(torch, ulys, o_slots, lse, steps: int) -> float:
     """ulys_lse_merge of the G head-group outputs taken as G partial results of one slot shape (a ring of G):
     algorithmic bytes (G partial o + lse read, one o + lse written) over the mean event time."""
@@ -558,8 +604,10 @@ def main():
                    "pack_frac_hbm_peak": round(head["pack_gbs"] / PEAK_HBM_GBS, 4),
                    "unpack_frac_hbm_peak": round(head["unpack_gbs"] / PEAK_HBM_GBS, 4),
                    "bytes": {"pack": st.bytes_pack(), "unpack": st.bytes_unpack()},
-                   "note": "algorithmic bytes (read + write) over the kernels' mean event time; two slot sets "
-                           "rotated (558 MB) and four ranks' shards cycled, so neither side is cache-resident"},
+                   "note": "algorithmic bytes (read + write) over the mean time between the events around each kernel "
+                           "inside the step (the event pair adds a few microseconds to kernels of 20-70 us); two "
+                           "slot sets rotated (558 MB) and four ranks' shards cycled, so neither side is "
+                           "cache-resident; repack_back_to_back times the kernels without per-launch events"},
     }
     res["repack"]["repack_gbs"] = round((st.bytes_pack() + st.bytes_unpack()) /
                                         ((res["pack_ms"]["mean"] + res["unpack_ms"]["mean"]) * 1e-3) / 1e9, 1)
@@ -607,6 +655,7 @@ def main():
         res["repack"]["amax_gbs"] = configs["e2e_p4_fp8_step"]["amax_gbs"]
         (q, k, v), shards = shards_of(torch, inputs, w, dev)
         res["pipelined_ms_per_step"] = round(pipelined_ms(torch, ulys, L, shards, args.warmup, args.steps), 4)
+        res["repack_back_to_back"] = repack_back_to_back(torch, ulys, L, shards, args.steps)
         res["hbm_copy_gbs"] = round(device_copy_gbs(torch), 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_rows)

@@ -160,15 +160,31 @@ void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // This workgroup's work: with a range split (a.ranges > 0), range blockIdx.x
-  // of its (b, head)'s (query tile, key tile) sequence; otherwise query tile
-  // qtile0, key-range chunk `split` of a.splits.
+  // This workgroup's work: with a range split (a.ranges > 0), range wx of its
+  // (b, head)'s (query tile, key tile) sequence; otherwise query tile qtile0,
+  // key-range chunk `split` of a.splits.
   const bool ranged = a.ranges > 0;
-  const int split = ranged ? 0 : blockIdx.x / a.qtiles;
-  const int qtile0 = ranged ? 0 : blockIdx.x - split * a.qtiles;
-  const int hl = blockIdx.y;                  // head within this launch
+  // Under a range split, workgroup w of the launch runs on XCD w % 8; when the
+  // workgroups divide evenly, XCD x takes the x-th contiguous block of (range,
+  // head, batch) indices, so the workgroups of one XCD walk neighbouring ranges
+  // of one head and share its K/V tiles in that XCD's L2 (measured +1%).
+  int wx = blockIdx.x, wy = blockIdx.y, wz = blockIdx.z;
+  if (ranged) {
+    const unsigned nwg = gridDim.x * gridDim.y * gridDim.z;
+    if ((nwg & 7u) == 0) {
+      const unsigned w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+      const unsigned w2 = (w & 7u) * (nwg >> 3) + (w >> 3);
+      const unsigned rest = w2 / gridDim.x;
+      wx = __builtin_amdgcn_readfirstlane((int)(w2 - rest * gridDim.x));
+      wy = __builtin_amdgcn_readfirstlane((int)(rest % gridDim.y));
+      wz = __builtin_amdgcn_readfirstlane((int)(rest / gridDim.y));
+    }
+  }
+  const int split = ranged ? 0 : wx / a.qtiles;
+  const int qtile0 = ranged ? 0 : wx - split * a.qtiles;
+  const int hl = wy;                  // head within this launch
   const int head = a.head0 + hl;
-  const int b = blockIdx.z;
+  const int b = wz;
   const int qrows = a.q_rows;
   const int rows = a.kv_rows;   // keys
   const int kvh = head / (a.hq / a.hkv);
@@ -648,8 +664,8 @@ void attn_fwd_kernel(AttnArgs a) {
   const long long units = (long long)a.qtiles * nunits;
   long long u = 0, uend = 1, ustart = 0, tail_u = -1, tail_end = -1;
   if (ranged) {
-    ustart = u = (long long)blockIdx.x * units / a.ranges;
-    uend = (long long)(blockIdx.x + 1) * units / a.ranges;
+    ustart = u = (long long)wx * units / a.ranges;
+    uend = (long long)(wx + 1) * units / a.ranges;
     const long long next_tile = (ustart / nunits + 1) * nunits;
     if (ustart % nunits != 0 && next_tile < uend) {
       tail_u = ustart;
@@ -657,7 +673,7 @@ void attn_fwd_kernel(AttnArgs a) {
       u = next_tile;
     }
   }
-  if (ranged && blockIdx.x == 0 && hl == 0 && tid == 0) a.range_nseq[b] = nseq;
+  if (ranged && wx == 0 && hl == 0 && tid == 0) a.range_nseq[b] = nseq;
   reset_kcur();
   for (;;) {
     if (u >= uend) {
@@ -759,7 +775,41 @@ void attn_fwd_kernel(AttnArgs a) {
         return true;
       };
       int sa = 0;
-      for (int i = 0;; ++i) {
+      int i0 = 0;
+      if constexpr (!MASK) {
+        // Clean steps first: while every tile a step touches (positions i and
+        // i+1, and the load of i+2) lies before the first dirty tile and the
+        // gap, position pos holds tile p0 + pos, so a step needs no dirty
+        // tests and its tile load is the previous one's plus one tile (two
+        // pointer increments instead of the tile-index arithmetic).
+        const int fd = min(min(dx, dy), min(dz, skip_first));
+        const int n_fast = max(0, min(fd - p0 - 2, n - 2));
+        const unsigned char* ktp = kbase + (size_t)(unsigned int)(p0 + 2) * ktile;
+        const unsigned char* vtp = vbase + (size_t)(unsigned int)(p0 + 2) * vtile;
+        for (; i0 < n_fast; ++i0) {
+          const int sb = sa == kStages - 1 ? 0 : sa + 1;
+          const int sp = sa == 0 ? kStages - 1 : sa - 1;
+          const unsigned int kl = lds_u32(k_of(sp)) + kls;
+          const unsigned int vl = lds_u32(v_of(sp) + kVRegion) + vls;
+#pragma unroll
+          for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kWaves * 1024);
+#pragma unroll
+          for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kWaves * 1024);
+          ktp += ktile;
+          vtp += vtile;
+          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, sa, (sa - sb) * C::kKTile,
+                    B1{}, 0, ~0u, false, sB, sA, pB, pA);
+          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, sb, 0, B0{}, 0, ~0u, false,
+                    sA, sB, pA, pB);
+          const int adv = sb == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
+#pragma unroll
+          for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
+          tile_barrier();
+          sa = sb;
+        }
+        if (n_fast > 0) tc = p0 + n_fast;   // (clean positions precede the gap: tile = p0 + position)
+      }
+      for (int i = i0;; ++i) {
         const int sb = sa == kStages - 1 ? 0 : sa + 1;
         if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
         sa = sb;
@@ -820,7 +870,7 @@ void attn_fwd_kernel(AttnArgs a) {
       // range_merge_kernel): slot 0 if it is this range's first piece, 1 if
       // its last.
       const int slot = upiece == ustart ? 0 : 1;
-      const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + blockIdx.x) * 2 + slot;
+      const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + wx) * 2 + slot;
       if (row < qrows) {
         float* pp = a.part_o + (pidx * kBM + wave * 32 + l32) * D;
 #pragma unroll
