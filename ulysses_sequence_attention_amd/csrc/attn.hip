@@ -786,28 +786,52 @@ void attn_fwd_kernel(AttnArgs a) {
         const int n_fast = max(0, min(fd - p0 - 2, n - 2));
         const unsigned char* ktp = kbase + (size_t)(unsigned int)(p0 + 2) * ktile;
         const unsigned char* vtp = vbase + (size_t)(unsigned int)(p0 + 2) * vtile;
-        for (; i0 < n_fast; ++i0) {
-          const int sb = sa == kStages - 1 ? 0 : sa + 1;
-          const int sp = sa == 0 ? kStages - 1 : sa - 1;
-          const unsigned int kl = lds_u32(k_of(sp)) + kls;
-          const unsigned int vl = lds_u32(v_of(sp) + kVRegion) + vls;
+        // One clean step: positions i (stage SA) and i+1 (stage SB), the load
+        // of position i+2 into SP.  The K read offsets point at stage 0 for the
+        // clean steps, so a read of stage s is the offset plus s * kKTile.
+        // With the stages compile-time constants (the unrolled rounds below)
+        // every LDS read and tile-load address is a register plus an immediate
+        // and the step has no address arithmetic at all (measured +2-3% at two
+        // and ten heads, +7% at one).
+        auto clean_step = [&](auto SA, auto SB, auto SP) ULYS_INLINE {
+          const unsigned int kl = lds_u32(k_of(SP)) + kls;
+          const unsigned int vl = lds_u32(v_of(SP) + kVRegion) + vls;
 #pragma unroll
           for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kWaves * 1024);
 #pragma unroll
           for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kWaves * 1024);
           ktp += ktile;
           vtp += vtile;
-          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, sa, (sa - sb) * C::kKTile,
-                    B1{}, 0, ~0u, false, sB, sA, pB, pA);
-          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, sb, 0, B0{}, 0, ~0u, false,
-                    sA, sB, pA, pB);
-          const int adv = sb == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
-#pragma unroll
-          for (int k = 0; k < kKOffs; ++k) kcur[k] += adv;
+          const int ka = int(SA) * C::kKTile, kbb = int(SB) * C::kKTile;
+          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B0{}, i, kf); }, SA, ka, B1{}, 0, ~0u,
+                    false, sB, sA, pB, pA);
+          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B1{}, i, kf); }, SB, kbb, B0{}, 0, ~0u,
+                    false, sA, sB, pA, pB);
           tile_barrier();
-          sa = sb;
+        };
+        if (n_fast > 0) {
+          static_assert(kStages == 3, "a clean round is three steps, one per stage");
+          using S0 = std::integral_constant<int, 0>;
+          using S1 = std::integral_constant<int, 1>;
+          using S2 = std::integral_constant<int, 2>;
+#pragma unroll
+          for (int k = 0; k < kKOffs; ++k) kcur[k] -= C::kKTile;   // (they pointed at stage 1 = sa + 1)
+          for (; i0 + kStages <= n_fast; i0 += kStages) {
+            clean_step(S0{}, S1{}, S2{});
+            clean_step(S1{}, S2{}, S0{});
+            clean_step(S2{}, S0{}, S1{});
+          }
+          for (; i0 < n_fast; ++i0) {   // the last steps short of a round
+            const int sb = sa == kStages - 1 ? 0 : sa + 1;
+            clean_step(sa, sb, sa == 0 ? kStages - 1 : sa - 1);
+            sa = sb;
+          }
+          // the step loop's K offsets point at the stage after sa
+          const int kfwd = (sa == kStages - 1 ? 0 : sa + 1) * C::kKTile;
+#pragma unroll
+          for (int k = 0; k < kKOffs; ++k) kcur[k] += kfwd;
+          tc = p0 + n_fast;   // (clean positions precede the gap: tile = p0 + position)
         }
-        if (n_fast > 0) tc = p0 + n_fast;   // (clean positions precede the gap: tile = p0 + position)
       }
       for (int i = i0;; ++i) {
         const int sb = sa == kStages - 1 ? 0 : sa + 1;
