@@ -982,8 +982,10 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(AttnArgs a) 
     a.lse[((size_t)b * a.hq + head) * a.q_rows + row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
-// Merge of a range split's cut tiles.  Workgroup: one (query tile, head, b).
-// The tile's pieces come from the non-empty ranges between the one holding
+// Merge of a range split's cut tiles.  Workgroup: kBM / kMergeGroupsPerTile
+// rows of one (query tile, head, b): several workgroups per tile, so that a
+// CU holds several of them and their dependent load phases (the pieces' LSEs,
+// then each piece's rows) overlap.  The tile's pieces come from the non-empty ranges between the one holding
 // its first unit and the one holding its last (range of unit x: the largest
 // r with r U / R <= x); a tile within one range was written by the attention
 // kernel and is skipped.  Combination in range order, as for key-range
@@ -991,12 +993,17 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(AttnArgs a) 
 // lse = (M + log2 sum_r w_r) ln 2.  Thread: 4 head dims of kRowsPerPass rows
 // (consecutive lanes read consecutive 16-byte chunks of a row), all of a
 // piece's loads issued before they are used.
+constexpr int kMergeGroupsPerTile = 4;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void range_merge_kernel(AttnArgs a) {
   constexpr int kC4 = D / 4;                     // 16-byte chunks per row
   constexpr int kRowsPerPass = kThreads / kC4;   // rows the workgroup covers at once
-  constexpr int kPasses = kBM / kRowsPerPass;
-  const int qtile = blockIdx.x, hl = blockIdx.y, b = blockIdx.z;
+  constexpr int kRowsPerGroup = kBM / kMergeGroupsPerTile;
+  constexpr int kPasses = kRowsPerGroup / kRowsPerPass;
+  static_assert(kPasses >= 1 && kRowsPerGroup % kRowsPerPass == 0, "whole passes per workgroup");
+  const int qtile = blockIdx.x / kMergeGroupsPerTile, hl = blockIdx.y, b = blockIdx.z;
+  const int rbase = (blockIdx.x % kMergeGroupsPerTile) * kRowsPerGroup;   // this workgroup's rows of the tile
   const long long nunits = max(a.range_nseq[b], 1);
   const long long units = (long long)a.qtiles * nunits, R = a.ranges;
   auto range_start = [&](long long r) { return r * units / R; };
@@ -1004,7 +1011,7 @@ __global__ __launch_bounds__(kThreads) void range_merge_kernel(AttnArgs a) {
   const long long t0 = (long long)qtile * nunits;
   const int rf = range_of(t0), rl = range_of(t0 + nunits - 1);
   if (rf == rl) return;   // (a range holds the whole tile)
-  const int c4 = threadIdx.x % kC4, r0 = threadIdx.x / kC4;
+  const int c4 = threadIdx.x % kC4, r0 = rbase + threadIdx.x / kC4;
   const size_t pbase = ((size_t)b * a.hsub + hl) * (size_t)R;
   auto piece = [&](int r) { return ((pbase + r) * 2 + (range_start(r) < t0 ? 1 : 0)) * kBM; };
   auto nonempty = [&](int r) { return range_start(r + 1) > range_start(r); };
@@ -1068,7 +1075,8 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ranges > 0) {
-    hipLaunchKernelGGL((range_merge_kernel<D>), dim3(a.qtiles, a.hsub, a.batch), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((range_merge_kernel<D>), dim3(a.qtiles * kMergeGroupsPerTile, a.hsub, a.batch),
+                       dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (a.splits == 1) return hipSuccess;
