@@ -54,6 +54,10 @@ def test_tiny_config_all_rows(gpu, rank, group):
     (1, 600, 2, 2, 64, [(226, 600)]),            # tail padding
     (1, 700, 2, 2, 128, [(0, 699)]),             # only the last key valid
     (1, 640, 2, 2, 128, [(64, 576)]),            # gap aligned to whole tiles
+    # a gap ending on a tile edge whose last tile is skipped, then a ragged last tile (whose keys past
+    # the end must still be masked): D = 128 and 64, and one per batch
+    (1, 1000, 2, 2, 128, [(100, 512)]),
+    (2, 700, 2, 1, 64, [(65, 256), (300, 640)]),
 ])
 def test_ragged_masked_gqa(gpu, b, rows, hq, hkv, d, gaps):
     w = inputs.small("case", 40 + rows, batch=b, s_local=rows, hq=hq, hkv=hkv, head_dim=d, q_mult=2.0)

@@ -48,6 +48,7 @@ SPLIT_CASES = [  # b, nq, nk, hq, hkv, d, splits, gaps
     (1, 1030, 3333, 2, 2, 128, 5, [(3300, 3333)]),
     (1, 1, 4100, 1, 1, 128, 4, None),            # one query row
     (2, 33, 65, 2, 2, 64, 2, None),              # two tiles, the second holding one key
+    (1, 500, 1000, 2, 2, 128, 3, [(100, 512)]),  # a skipped tile-aligned gap end, then a ragged last tile
 ]
 
 

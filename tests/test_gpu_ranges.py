@@ -54,6 +54,7 @@ RANGE_CASES = [  # b, nq, nk, hq, hkv, d, ranges, gaps
     (3, 100, 1000, 2, 2, 64, 20, None),             # 16 units in 20 runs: 4 runs empty
     (1, 2, 33, 2, 2, 128, 32, None),                # one unit: 31 empty runs, one whole tile
     (1, 1030, 3333, 2, 2, 128, 9, [(3300, 3333)]),  # ragged last query tile and key tile
+    (1, 500, 1000, 2, 2, 128, 6, [(100, 512)]),     # a skipped tile-aligned gap end, then a ragged last tile
 ]
 
 

@@ -728,18 +728,17 @@ void attn_fwd_kernel(AttnArgs a) {
         read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
       }
       int tc = seq_tile(0);
-      // Tiles with keys outside [0, rows) or inside the gap: the one holding the
-      // gap's first key, the one holding its last, and the ragged last tile
-      // (ascending; tiles are visited in ascending order, so one compare per
-      // tile against the next of them decides whether its blocks take the
-      // per-block range test).
+      // Visited tiles with keys outside [0, rows) or inside the gap ("dirty":
+      // their blocks take the per-block range test): the one holding the gap's
+      // first key, the one holding its last, and the ragged last tile.  Each
+      // visited tile is compared with all three (the gap's last tile may be
+      // wholly inside the gap and never visited, so no running "next dirty
+      // tile" can be kept).
       constexpr int kNone = 0x7fffffff;
       const int dz = tail_tile >= 0 ? tail_tile : kNone;
       const int dx = gs < ge ? gs / kBN : dz, dy = gs < ge ? (ge - 1) / kBN : dz;
-      auto next_dirty = [&](int t) { return dx > t ? dx : dy > t ? dy : dz > t ? dz : kNone; };
-      int nd = next_dirty(tc - 1);
-      bool dc = tc == nd;
-      if (dc) nd = next_dirty(tc);
+      auto is_dirty = [&](int t) { return t == dx || t == dy || t == dz; };
+      bool dc = is_dirty(tc);
       // mask words of the tile's second block (mw1) and of the next tile's blocks
       // (fetched a block ahead: each is a scalar value once it is used)
       unsigned mw1 = mask_word(tc * kBN + 32);
@@ -763,8 +762,7 @@ void attn_fwd_kernel(AttnArgs a) {
         if (i + 1 >= n) return false;
         tc = tn;
         mw1 = wn1;
-        dc = tc == nd;
-        if (dc) nd = next_dirty(tc);
+        dc = is_dirty(tc);
         iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
                   __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
         // the next step reads K from the stage after SB
@@ -775,65 +773,80 @@ void attn_fwd_kernel(AttnArgs a) {
         return true;
       };
       int sa = 0;
-      int i0 = 0;
-      if constexpr (!MASK) {
-        // Clean steps first: while every tile a step touches (positions i and
-        // i+1, and the load of i+2) lies before the first dirty tile and the
-        // gap, position pos holds tile p0 + pos, so a step needs no dirty
-        // tests and its tile load is the previous one's plus one tile (two
-        // pointer increments instead of the tile-index arithmetic).
-        const int fd = min(min(dx, dy), min(dz, skip_first));
-        const int n_fast = max(0, min(fd - p0 - 2, n - 2));
-        const unsigned char* ktp = kbase + (size_t)(unsigned int)(p0 + 2) * ktile;
-        const unsigned char* vtp = vbase + (size_t)(unsigned int)(p0 + 2) * vtile;
-        // One clean step: positions i (stage SA) and i+1 (stage SB), the load
-        // of position i+2 into SP.  The K read offsets point at stage 0 for the
-        // clean steps, so a read of stage s is the offset plus s * kKTile.
-        // With the stages compile-time constants (the unrolled rounds below)
-        // every LDS read and tile-load address is a register plus an immediate
-        // and the step has no address arithmetic at all (measured +2-3% at two
-        // and ten heads, +7% at one).
-        auto clean_step = [&](auto SA, auto SB, auto SP) ULYS_INLINE {
-          const unsigned int kl = lds_u32(k_of(SP)) + kls;
-          const unsigned int vl = lds_u32(v_of(SP) + kVRegion) + vls;
+      // Clean steps: while every tile a step touches (positions i and i+1, and
+      // the load of i+2) is clean and on one side of the gap, consecutive
+      // positions hold consecutive tiles, so a step needs no dirty tests and
+      // its tile load is the previous one's plus one tile (two pointer
+      // increments instead of the tile-index arithmetic).  The steps of a
+      // clean run take the K read offsets at stage 0, so a read of stage s is
+      // the offset plus s * kKTile; in whole ring rounds the stages are
+      // compile-time constants, and every LDS read and tile-load address is a
+      // register plus an immediate with no address arithmetic at all
+      // (measured +2-3% at two and ten heads, +7% at one).
+      const unsigned char* ktp = kbase;
+      const unsigned char* vtp = vbase;
+      auto clean_step = [&](auto SA, auto SB, auto SP) ULYS_INLINE {
+        const unsigned int kl = lds_u32(k_of(SP)) + kls;
+        const unsigned int vl = lds_u32(v_of(SP) + kVRegion) + vls;
 #pragma unroll
-          for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kWaves * 1024);
+        for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kWaves * 1024);
 #pragma unroll
-          for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kWaves * 1024);
-          ktp += ktile;
-          vtp += vtile;
-          const int ka = int(SA) * C::kKTile, kbb = int(SB) * C::kKTile;
-          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B0{}, i, kf); }, SA, ka, B1{}, 0, ~0u,
-                    false, sB, sA, pB, pA);
-          iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B1{}, i, kf); }, SB, kbb, B0{}, 0, ~0u,
-                    false, sA, sB, pA, pB);
-          tile_barrier();
-        };
-        if (n_fast > 0) {
-          static_assert(kStages == 3, "a clean round is three steps, one per stage");
-          using S0 = std::integral_constant<int, 0>;
-          using S1 = std::integral_constant<int, 1>;
-          using S2 = std::integral_constant<int, 2>;
+        for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kWaves * 1024);
+        ktp += ktile;
+        vtp += vtile;
+        const int ka = int(SA) * C::kKTile, kbb = int(SB) * C::kKTile;
+        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B0{}, i, kf); }, SA, ka, B1{}, 0, ~0u,
+                  false, sB, sA, pB, pA);
+        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B1{}, i, kf); }, SB, kbb, B0{}, 0, ~0u,
+                  false, sA, sB, pA, pB);
+        tile_barrier();
+      };
+      // Clean steps from step i: the first tile at or after step i's that is
+      // dirty, or the side of the gap ending, ends the run (no key mask: with
+      // one, positions follow the tile list).
+      auto clean_run = [&](int i) -> int {
+        if constexpr (MASK) return 0;
+        const int room = n - 2 - i;   // steps whose tile load stays inside the piece
+        const int q = p0 + i;
+        int t0, tend;
+        if (q + 2 < skip_first) { t0 = q; tend = skip_first; }        // before the gap
+        else if (q >= skip_first) { t0 = q + nskip; tend = ntiles; }   // after it
+        else return 0;                                                   // the step crosses it
+        const int d = dx >= t0 ? dx : dy >= t0 ? dy : dz >= t0 ? dz : kNone;   // (dx <= dy <= dz)
+        return max(0, min(room, min(tend, d) - t0 - 2));
+      };
+      // Whole ring rounds of clean steps from step i (the ring at stage 0,
+      // so sa = 0 and the K offsets point at stage 1); the steps short of a
+      // round take the general step.
+      auto run_clean = [&](int i, int rounds) {
+        static_assert(kStages == 3, "a clean round is three steps, one per stage");
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        ktp = kbase + (size_t)(unsigned int)seq_tile(i + 2) * ktile;
+        vtp = vbase + (size_t)(unsigned int)seq_tile(i + 2) * vtile;
 #pragma unroll
-          for (int k = 0; k < kKOffs; ++k) kcur[k] -= C::kKTile;   // (they pointed at stage 1 = sa + 1)
-          for (; i0 + kStages <= n_fast; i0 += kStages) {
-            clean_step(S0{}, S1{}, S2{});
-            clean_step(S1{}, S2{}, S0{});
-            clean_step(S2{}, S0{}, S1{});
-          }
-          for (; i0 < n_fast; ++i0) {   // the last steps short of a round
-            const int sb = sa == kStages - 1 ? 0 : sa + 1;
-            clean_step(sa, sb, sa == 0 ? kStages - 1 : sa - 1);
-            sa = sb;
-          }
-          // the step loop's K offsets point at the stage after sa
-          const int kfwd = (sa == kStages - 1 ? 0 : sa + 1) * C::kKTile;
-#pragma unroll
-          for (int k = 0; k < kKOffs; ++k) kcur[k] += kfwd;
-          tc = p0 + n_fast;   // (clean positions precede the gap: tile = p0 + position)
+        for (int k = 0; k < kKOffs; ++k) kcur[k] -= C::kKTile;
+        for (int r = 0; r < rounds; ++r) {
+          clean_step(S0{}, S1{}, S2{});
+          clean_step(S1{}, S2{}, S0{});
+          clean_step(S2{}, S0{}, S1{});
         }
-      }
-      for (int i = i0;; ++i) {
+#pragma unroll
+        for (int k = 0; k < kKOffs; ++k) kcur[k] += C::kKTile;
+        tc = seq_tile(i + rounds * kStages);
+        dc = is_dirty(tc);
+      };
+      for (int i = 0;; ++i) {
+        if constexpr (!MASK) {
+          if (sa == 0) {
+            const int rounds = clean_run(i) / kStages;
+            if (rounds > 0) {
+              run_clean(i, rounds);
+              i += rounds * kStages;
+            }
+          }
+        }
         const int sb = sa == kStages - 1 ? 0 : sa + 1;
         if (!step(i, sa, sb, sa == 0 ? kStages - 1 : sa - 1)) break;
         sa = sb;
