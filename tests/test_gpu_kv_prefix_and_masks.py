@@ -278,3 +278,27 @@ def test_mask_at_the_key_limit(gpu):
     rows = sample_rows(nq, every=16, extra=16)
     o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(d), rows=rows, key_mask=m)
     check_attention(o, l, o_ref, l_ref, rows=rows, label="262144 keys")
+
+
+@pytest.mark.parametrize("splits", [0, 3, -6])
+def test_mask_bits_past_the_last_key_are_ignored(gpu, splits):
+    """The header's rule: bits of the last mask word for keys j >= kv_rows are ignored.  The words here have
+    every such bit set (the last word all ones), with a ragged key count and a gap whose end is a tile edge
+    (so its last tile is skipped); the result must be the oracle's over the real keys only, without a split,
+    under a key-range split and under a range split."""
+    b, nq, nk, hq, hkv, d = 1, 300, 1000, 2, 2, 128
+    q = bits(inputs.random_bf16((b, nq, hq, d), 91))
+    k = bits(inputs.random_bf16((b, nk, hkv, d), 92))
+    v = bits(inputs.random_bf16((b, nk, hkv, d), 93))
+    m = inputs.random_key_mask(b, nk, 94, 0.8)
+    m[:, 960:] = True                                   # the last 64-key tile: every real key valid
+    words = inputs.key_mask_words(m)
+    words[:, -1] = -1                                   # ... and the 24 bits past the 1000th key set too
+    gaps = [(100, 512)]
+    o = torch.full((b, nq, hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    l = torch.full((b, hq, nq), float("nan"), dtype=torch.float32, device="cuda")
+    gpu.ulys_attend_group_ex(from_bits(q), from_bits(k), from_bits(v), o, l, key_gaps=gaps, key_mask=words.cuda(),
+                             key_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(d), gaps, key_mask=m)
+    check_attention(o, l, o_ref, l_ref, label=f"mask bits past the end, splits {splits}")
