@@ -13,6 +13,13 @@ from ulysses_sequence_attention_amd import inputs
 O_MAX_ABS = 2e-2
 O_MEAN_ABS = 1e-3
 LSE_MAX_ABS = 1e-3
+# A second, tighter LSE check for bf16 q/k, derived from the arithmetic rather than stated: the kernel's lse is m + log2 of
+# an fp32 sum of unrounded probabilities (scores are exact bf16 products summed in fp32), so it differs from
+# the fp64 oracle by fp32 rounding only -- at most 3.3e-6 over plain, ragged, gap, mask, split, D = 64, peaky
+# GQA (q x 4) and full-size Wan and joint shapes.  5e-5 leaves 15x of that and still catches a wrong key set
+# whose effect on the LSE hides under the stated 1e-3 (one duplicated key among 33k moves it by 3e-5 x weight;
+# eight moved it by 2.4e-4).
+LSE_ARITH_ABS = 5e-5
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -44,10 +51,12 @@ def shards_of(w: inputs.Workload, seed=None):
     return (q, k, v), out
 
 
-def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, label=""):
+def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, label="", fp8=False):
     """Assert the bf16 output and fp32 LSE of the GPU are within tolerance of the fp64 oracle.
 
-    ``rows``: the query rows the oracle computed (the GPU arrays hold all rows)."""
+    ``rows``: the query rows the oracle computed (the GPU arrays hold all rows).  ``fp8``: e4m3 q/k, whose
+    MFMA accumulates the code products with more rounding than fp32 (up to 6.4e-5 of LSE on a peaky masked
+    case), so only the stated LSE bar applies."""
     og = f64(o_gpu)
     lg = f64(lse_gpu)
     if rows is not None:
@@ -60,6 +69,8 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, label=""):
     assert stats["o_max"] <= O_MAX_ABS, f"{label}: {stats}"
     assert stats["o_mean"] <= O_MEAN_ABS, f"{label}: {stats}"
     assert stats["lse_max"] <= LSE_MAX_ABS, f"{label}: {stats}"
+    if not fp8:
+        assert stats["lse_max"] <= LSE_ARITH_ABS, f"{label}: lse beyond fp32 rounding: {stats}"
     return stats
 
 

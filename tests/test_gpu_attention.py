@@ -204,7 +204,7 @@ def test_fp8_attention_vs_oracle_on_decoded_codes(gpu, d, rows, gaps):
                    fp8=True, amax=amax)
     c = ofp8.score_scale(oatt.default_scale(d), sq, sk)
     o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), vt.double().numpy(), float(c), gaps)
-    check_attention(o, l, o_ref, l_ref, label=f"fp8 d{d}")
+    check_attention(o, l, o_ref, l_ref, label=f"fp8 d{d}", fp8=True)
 
 
 def test_e2e_p4_fp8_pipeline(gpu):

@@ -134,7 +134,7 @@ def test_e2e_p4_fp8_five_groups_equal_one_call(gpu, e2e):
         o_ref, l_ref = oatt.attention(qd, kd, vt[:, :, heads].double().numpy(), c, rows=rows)
         got_o = np.concatenate([f64(s) for s in out1], axis=1)[:, rows][:, :, heads]
         got_l = f64(lse1[rank].reshape(1, 10, -1))[:, [h - 10 * rank for h in heads]][:, :, rows]
-        check_attention(got_o, got_l, o_ref, l_ref, label=f"e2e fp8 rank {rank}")
+        check_attention(got_o, got_l, o_ref, l_ref, label=f"e2e fp8 rank {rank}", fp8=True)
 
 
 def test_tiny_reading_b_four_heads_per_rank(gpu):

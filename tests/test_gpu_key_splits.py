@@ -145,7 +145,7 @@ def test_fp8_with_splits(gpu):
                 fp8=True, amax=amax)
     c = ofp8.score_scale(oatt.default_scale(d), sq, sk)
     o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), vt.double().numpy(), float(c), [(10, 300)])
-    check_attention(o, l, o_ref, l_ref, label="fp8 splits 3")
+    check_attention(o, l, o_ref, l_ref, label="fp8 splits 3", fp8=True)
 
 
 def test_splits_heads_in_several_launches(gpu):

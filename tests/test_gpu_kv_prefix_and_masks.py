@@ -263,7 +263,7 @@ def test_mask_fp8_qk(gpu):
     torch.cuda.synchronize()
     c = float(ofp8.score_scale(oatt.default_scale(d), sq, sk))
     o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), _as_f64(v), c, key_mask=m)
-    check_attention(o, l, o_ref, l_ref, label="fp8 + mask")
+    check_attention(o, l, o_ref, l_ref, label="fp8 + mask", fp8=True)
 
 
 def test_mask_at_the_key_limit(gpu):

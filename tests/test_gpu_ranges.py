@@ -142,7 +142,7 @@ def test_fp8_with_ranges(gpu):
                 fp8=True, amax=amax)
     c = ofp8.score_scale(oatt.default_scale(d), sq, sk)
     o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), vt.double().numpy(), float(c), [(10, 300)])
-    check_attention(o, l, o_ref, l_ref, label="fp8 ranges 6")
+    check_attention(o, l, o_ref, l_ref, label="fp8 ranges 6", fp8=True)
 
 
 def test_ranges_wan_shape_sampled_rows(gpu):
@@ -209,4 +209,4 @@ def test_ranges_gqa_mask_fp8_d64(gpu):
                 fp8=True, amax=amax)
     c = ofp8.score_scale(oatt.default_scale(d), sq, sk)
     o_ref, l_ref = oatt.attention(ofp8.decode(qc), ofp8.decode(kc), v.double().numpy(), float(c), key_mask=mask)
-    check_attention(o, l, o_ref, l_ref, label="GQA fp8 mask ranges 11")
+    check_attention(o, l, o_ref, l_ref, label="GQA fp8 mask ranges 11", fp8=True)
