@@ -288,8 +288,9 @@ int ulys_attend_group(int batch, int rows, int hq, int hkv, int head_dim,
  * workspace, the same kernels and the same bytes.
  *
  * The split partials live in a static device array of the library, 128 MiB
- * per GPU, held from the first call on that GPU until the process ends; the call itself allocates nothing.  A call whose heads
- * need more than the array runs them in several launches (as a small
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call itself allocates nothing.  A call whose heads need more than the
+ * array runs them in several launches (as a small
  * workspace does for ulys_attend_group); one whose single head needs more is
  * ULYS_EINVAL with nothing enqueued.  Every call on a GPU shares that GPU's
  * array: calls that overlap on one GPU (different streams, no ordering
