@@ -59,6 +59,24 @@ def test_joint_varlen_groups_equal_full_call(gpu):
     check_attention(of, lf, o_ref, l_ref, rows=rows, label="joint varlen, 12 heads")
 
 
+
+def test_joint_varlen_masked_kv_adversarial(gpu):
+    """Joint text+image workload at full size, one 4-head group: replacing the masked keys' K by +1e4 and
+    V by -1e4 (keys [226, 512)) leaves o and lse byte for byte the same (masked keys take no part, under
+    the automatic range split of this shape)."""
+    w = inputs.JOINT_VARLEN
+    q, k, v = [bits(x) for x in inputs.global_qkv(w)]
+    gh = w.hq // w.groups
+    q, k, v = (np.ascontiguousarray(x[:, :, :gh]) for x in (q, k, v))
+    gaps = [w.key_gap]
+    o1, l1 = _attend(gpu, from_bits(q), from_bits(k), from_bits(v), gaps=gaps)
+    k2, v2 = _as_f64(k).copy(), _as_f64(v).copy()
+    k2[:, w.key_gap[0]:w.key_gap[1]] = 1e4
+    v2[:, w.key_gap[0]:w.key_gap[1]] = -1e4
+    o2, l2 = _attend(gpu, from_bits(q), torch.from_numpy(k2).to(torch.bfloat16).cuda(),
+                     torch.from_numpy(v2).to(torch.bfloat16).cuda(), gaps=gaps)
+    assert _same(o1, o2) and _same(l1, l2)
+
 def test_gqa_groups_equal_full_call(gpu):
     """GQA workload at full size (batch 2, 16384 rows, 16 q heads over 4 kv heads, q x 2): the unsplit
     16-head call equals its four groups of 4 q heads over 1 kv head byte for byte; sampled rows of every
