@@ -209,6 +209,15 @@ def shards_of(torch, inputs, w, dev):
     return (q, k, v), out
 
 
+def input_sha256(torch, tensors) -> str:
+    """SHA-256 of the seeded inputs' bytes (q, then k, then v), so a run's data can be checked to be the same."""
+    import hashlib
+    h = hashlib.sha256()
+    for x in tensors:
+        h.update(x.contiguous().view(torch.int16).numpy().tobytes())
+    return h.hexdigest()
+
+
 def run_config(torch, ulys, args, stream, L, shards, flops_step, peak, kernel, gaps=None, fp8=False,
                amax_each_step=False, traffic=None, extra=None):
     """Time RankStep over the config; returns the JSON object for it (attention roofline included)."""
@@ -594,7 +603,7 @@ def main():
                                f"slot(s) [1,27280,{L.gq},128] -> attention N=27280 D=128 non-causal + LSE -> unpack",
                    "batch": 1, "seq_len": rows, "heads_per_gpu": H // P, "head_dim": D, "head_groups": G,
                    "ulysses_degree_simulated": P, "schedule": "one stream, sequential",
-                   "slot_sets_rotated": 2},
+                   "slot_sets_rotated": 2, "input_sha256": input_sha256(torch, (q, k, v))},
         "roofline": head.pop("roofline"),
         "step_ms": head["step_ms"],
         "attention_tflops": head["attention_tflops"],
