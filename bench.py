@@ -103,14 +103,19 @@ def attention_roofline(flops_launch, launch_ms, peak, kernel, traffic=None, **ex
 
 
 def kernel_source_hash() -> str:
-    """Hash of the attention kernel's sources and compile flags: counters taken on another version of the
-    kernel are not reported as its traffic."""
+    """Hash of the attention kernel's code and compile flags: counters taken on another version of the
+    kernel are not reported as its traffic.  Comments and whitespace are left out, so a change of comment
+    text alone keeps the counters."""
     import hashlib
+    import re
     from ulysses_sequence_attention_amd import build as ubuild
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)    # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     h.update(" ".join(ubuild.FLAGS + ubuild.SOURCE_FLAGS.get("attn.hip", [])).encode())
     return h.hexdigest()
 

@@ -41,6 +41,13 @@
 //    MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
+//  * Steps over clean tiles (no key past the end or in the gap) run in whole
+//    ring rounds with the stages compile-time constants: every LDS read and
+//    tile-load address is then a register plus an immediate, with no address
+//    arithmetic in the step.
+//  * Under a range split the workgroups are ordered so that each XCD takes a
+//    contiguous block of (range, head) indices, sharing a head's K/V in its
+//    L2.
 //  * Work per workgroup: one query tile over all its key tiles; or, under a
 //    key-range split, a contiguous run of them; or, under a range split, a
 //    run of its (b, h)'s (query tile, key tile) sequence, walked as pieces.
