@@ -33,7 +33,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 # e4m3 q/k: the QK^T half of the FLOPs at the fp8 rate, the PV half at the bf16 rate
 PEAK_FP8_QK_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-ATTN_KERNEL = "attn_fwd_kernel<128, false, false>"   # D = 128, bf16 q/k, no key mask
+ATTN_KERNEL = "attn_fwd_kernel<128, false, false, 2>"   # D = 128, bf16 q/k, no key mask (two row halves per wave)
 MERGE_KERNEL = "range_merge_kernel<128>"             # the range split's merge, when the call uses one
 METRIC = "attention TFLOP/s + % MFMA peak at N=27280,H=10,D=128 bf16; repack GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
@@ -641,7 +641,7 @@ def main():
         print(json.dumps({"progress": "single call"}), file=sys.stderr, flush=True)
         # the fp8 whole step: amax + e4m3 pack + attention + unpack
         r, st8 = run_config(torch, ulys, args, stream, L, shards, flops_step, PEAK_FP8_QK_TFLOPS,
-                            "attn_fwd_kernel<128, true, false>" + (" + " + MERGE_KERNEL if res["roofline"]["range_split"]
+                            "attn_fwd_kernel<128, true, false, 1>" + (" + " + MERGE_KERNEL if res["roofline"]["range_split"]
                                                                    else ""),
                             fp8=True, amax_each_step=True,
                             extra={"note": "e4m3 q/k (QK^T at the fp8 rate), bf16 V and P; peak = the mixed bound "

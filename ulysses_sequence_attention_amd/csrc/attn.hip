@@ -6,8 +6,25 @@
 // lse_i = ln sum_J exp(s_ij); kv head = h / (hq / hkv) (GQA).
 //
 // How (MI355X-first):
-//  * One workgroup = 256 query rows of one (b, h): 8 waves of 32 rows, two
-//    waves per SIMD.  All waves share the K/V tiles in LDS.
+//  * One workgroup = 256 query rows of one (b, h); all its waves share the K/V
+//    tiles in LDS.  Two wave shapes (NH = row halves per wave):
+//     - bf16 q/k, head_dim 128, no key mask (NH = 2): 4 waves of 64 rows, one
+//       wave per SIMD.  Every K and V fragment read from LDS feeds the MFMAs of
+//       both 32-row halves, which halves the LDS bytes per MFMA.  O (128 regs)
+//       and Q (64) live in AGPRs, so the two contractions are inline-asm MFMAs
+//       (AGPR accumulator for PV, AGPR B operand for QK^T), and the loop body
+//       is placed by hand: one MFMA per issue group with one probability
+//       element beside it (scaled score, exponential, sum-and-pack three
+//       groups deep), an LDS read or a tile load beside every other one.  The
+//       compiler sees neither these MFMAs' latency nor their operands'
+//       hazards, so the waits are placed here: an MFMA result is read by VALU
+//       no sooner than 12 wait states after the MFMA (the count the compiler
+//       itself inserts on gfx950), and an operand written by VALU is read by an
+//       MFMA no sooner than 2 wait states after the write.
+//     - otherwise (fp8 q/k, head_dim 64, a key mask; NH = 1): 8 waves of 32
+//       rows, two waves per SIMD, builtin MFMAs.
+//    Both shapes do the same arithmetic per row in the same order, so their
+//    outputs are bit-identical.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (or the fp8 v_mfma_scale_f32_32x32x64_f8f6f4 for e4m3 q/k): in the
 //    accumulator every lane then holds ONE query row and 16 keys, so row max
@@ -26,7 +43,9 @@
 //  * Software pipeline over 32-key blocks: while block b's probabilities are
 //    formed (VALU), the wave issues the PV MFMAs of block b-1 and the QK^T
 //    MFMAs of block b+1, which do not depend on them; K operands of b+1 and V
-//    operands of b are read from LDS one phase before their MFMAs.
+//    operands of b are read from LDS one phase before their MFMAs.  With one
+//    wave per SIMD the clean steps also spread their tile loads over the PV
+//    MFMAs of their first block instead of issuing them in one burst.
 //  * Online softmax in the exp2 domain per 32-key block with a lazy max: the
 //    probabilities of a block are formed speculatively with the current
 //    running max, and the max is only raised (O, l rescaled, the block's
@@ -98,10 +117,12 @@ struct Cfg {
   static constexpr int kDB = D / 32;                     // 32-wide head_dim blocks of O
   static constexpr int kKSegs = kKTile / 1024;          // 1 KB LDS segments per tile
   static constexpr int kVSegs = kVTile / 1024;
-  static constexpr int kKSegsPerWave = (kKSegs + kWaves - 1) / kWaves;
-  static constexpr int kVSegsPerWave = (kVSegs + kWaves - 1) / kWaves;
-  static constexpr int kLoadsPerTile = kKSegsPerWave + kVSegsPerWave;   // per wave
 };
+
+// Row halves of 32 query rows per wave: two (one wave per SIMD, O and Q in
+// AGPRs) for bf16 q/k at head_dim 128 without a key mask, else one.
+template <int D, bool FP8, bool MASK>
+constexpr int kRowHalves = (D == 128 && !FP8 && !MASK) ? 2 : 1;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
@@ -143,10 +164,17 @@ __device__ __forceinline__ unsigned int lds_u32(const void* p) {
   return (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D, bool FP8, bool MASK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+template <int D, bool FP8, bool MASK, int NH>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads / NH, kThreads / NH), amdgpu_waves_per_eu(3 - NH, 3 - NH)))
 void attn_fwd_kernel(AttnArgs a) {
   using C = Cfg<D, FP8>;
+  static_assert(NH == kRowHalves<D, FP8, MASK>, "wave shape");
+  // NH row halves of 32 query rows per wave, kW waves per workgroup (kBM rows)
+  constexpr int kW = kWaves / NH;
+  constexpr int kT = kW * 64;
+  constexpr int kKSegsPerWave = (C::kKSegs + kW - 1) / kW;   // 1 KB tile-load segments per wave
+  constexpr int kVSegsPerWave = (C::kVSegs + kW - 1) / kW;
+  constexpr int kLoadsPerTile = kKSegsPerWave + kVSegsPerWave;
   // One LDS array per stage, selected at compile time: the compiler can then
   // prove that the DMA filling one stage never aliases reads of the other and
   // does not wait for in-flight tile loads before every LDS read.
@@ -216,7 +244,8 @@ void attn_fwd_kernel(AttnArgs a) {
   const size_t q_row_stride = (size_t)a.hq * D;            // elements
   const size_t kv_row_stride = (size_t)a.hkv * D;
   constexpr int kQRegs = FP8 ? 8 : 4;                       // dwords per fragment
-  unsigned int qf[C::kQKSteps][kQRegs];
+  unsigned int qf[NH][C::kQKSteps][kQRegs];
+  u32x4 qa[NH][C::kQKSteps];   // two row halves: Q operands as whole AGPR tuples
   // The thread index as a value the compiler cannot see through: per-lane
   // addresses of the per-piece work (Q loads, output writes, merge) are
   // formed from it inside the piece loop instead of being hoisted out of it
@@ -228,7 +257,9 @@ void attn_fwd_kernel(AttnArgs a) {
   };
   auto load_q = [&](int qrow0) {
     const int ft = fresh_tid();
-    const int row = qrow0 + (ft & 31), hh = (ft >> 5) & 1;
+#pragma unroll
+    for (int rh = 0; rh < NH; ++rh) {
+    const int row = qrow0 + rh * 32 + (ft & 31), hh = (ft >> 5) & 1;
     const unsigned char* qp = (const unsigned char*)a.q +
         (((size_t)b * qrows + row) * q_row_stride + (size_t)head * D) * C::kQKBytes;
 #pragma unroll
@@ -238,9 +269,16 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int part = 0; part < kQRegs / 4; ++part) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (row < qrows) x = ld16(qp + off + part * 16);
-        qf[kk][part * 4 + 0] = x.x; qf[kk][part * 4 + 1] = x.y;
-        qf[kk][part * 4 + 2] = x.z; qf[kk][part * 4 + 3] = x.w;
+        if constexpr (NH == 2) {
+          // copied into an AGPR tuple once per piece; the wait states cover the
+          // write before the first QK^T MFMA reads it
+          asm volatile("s_nop 4" : "=a"(qa[rh][kk]) : "0"(x));
+        } else {
+        qf[rh][kk][part * 4 + 0] = x.x; qf[rh][kk][part * 4 + 1] = x.y;
+        qf[rh][kk][part * 4 + 2] = x.z; qf[rh][kk][part * 4 + 3] = x.w;
+        }
       }
+    }
     }
   };
 
@@ -264,9 +302,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // first offset is per lane and the others move the scalar base.  With fewer
   // segments than waves (one load each), a surplus wave repeats the last
   // segment, which keeps every wave's load count per tile the same.
-  static_assert(C::kKSegsPerWave == 1 || C::kKSegs % kWaves == 0, "whole segments per wave");
-  static_assert(C::kVSegsPerWave == 1 || C::kVSegs % kWaves == 0, "whole segments per wave");
-  static_assert((kWaves * kKRowsPerSeg) % C::kKSwz == 0 && (kWaves * kVRowsPerSeg) % 4 == 0, "swizzle period");
+  static_assert(kKSegsPerWave == 1 || C::kKSegs % kW == 0, "whole segments per wave");
+  static_assert(kVSegsPerWave == 1 || C::kVSegs % kW == 0, "whole segments per wave");
+  static_assert((kW * kKRowsPerSeg) % C::kKSwz == 0 && (kW * kVRowsPerSeg) % 4 == 0, "swizzle period");
   const int kseg = min(wave, C::kKSegs - 1), vseg = min(wave, C::kVSegs - 1);
   const int kkey = kseg * kKRowsPerSeg + lane / C::kKChunks;
   const int kck = (lane % C::kKChunks) ^ (kkey & (C::kKSwz - 1));
@@ -278,11 +316,11 @@ void attn_fwd_kernel(AttnArgs a) {
   const unsigned int vls = __builtin_amdgcn_readfirstlane(vseg * 1024);
   const unsigned int ktile = kBN * krow, vtile = kBN * vrow;   // bytes per tile (hq <= 65535: fits)
   const int tail_tile = last_rows < kBN ? ntiles - 1 : -1;
-  unsigned int kgo_u[C::kKSegsPerWave], vgo_u[C::kVSegsPerWave];
+  unsigned int kgo_u[kKSegsPerWave], vgo_u[kVSegsPerWave];
 #pragma unroll
-  for (int u = 0; u < C::kKSegsPerWave; ++u) kgo_u[u] = kgo + u * kWaves * kKRowsPerSeg * krow;
+  for (int u = 0; u < kKSegsPerWave; ++u) kgo_u[u] = kgo + u * kW * kKRowsPerSeg * krow;
 #pragma unroll
-  for (int u = 0; u < C::kVSegsPerWave; ++u) vgo_u[u] = vgo + u * kWaves * kVRowsPerSeg * vrow;
+  for (int u = 0; u < kVSegsPerWave; ++u) vgo_u[u] = vgo + u * kW * kVRowsPerSeg * vrow;
   auto load_tile = [&](int j, auto st) {
     const unsigned int kl = lds_u32(k_of(st)) + kls;
     const unsigned int vl = lds_u32(v_of(st) + kVRegion) + vls;
@@ -298,39 +336,58 @@ void attn_fwd_kernel(AttnArgs a) {
       const unsigned int kc = ((ln % C::kKChunks) ^ (kr & (C::kKSwz - 1))) * 16;
       const unsigned int vc = (vswz<D>(vr, 2 * (ln % C::kVChunks)) >> 1) * 16;
 #pragma unroll
-      for (int u = 0; u < C::kKSegsPerWave; ++u)
-        dma16(kt, min(kr + u * kWaves * kKRowsPerSeg, last_rows - 1) * krow + kc, kl + u * kWaves * 1024);
+      for (int u = 0; u < kKSegsPerWave; ++u)
+        dma16(kt, min(kr + u * kW * kKRowsPerSeg, last_rows - 1) * krow + kc, kl + u * kW * 1024);
 #pragma unroll
-      for (int u = 0; u < C::kVSegsPerWave; ++u)
-        dma16(vt, min(vr + u * kWaves * kVRowsPerSeg, last_rows - 1) * vrow + vc, vl + u * kWaves * 1024);
+      for (int u = 0; u < kVSegsPerWave; ++u)
+        dma16(vt, min(vr + u * kW * kVRowsPerSeg, last_rows - 1) * vrow + vc, vl + u * kW * 1024);
     } else {
 #pragma unroll
-      for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(kt, kgo_u[u], kl + u * kWaves * 1024);
+      for (int u = 0; u < kKSegsPerWave; ++u) dma16(kt, kgo_u[u], kl + u * kW * 1024);
 #pragma unroll
-      for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vt, vgo_u[u], vl + u * kWaves * 1024);
+      for (int u = 0; u < kVSegsPerWave; ++u) dma16(vt, vgo_u[u], vl + u * kW * 1024);
     }
   };
 
   // ---- running state ----
   // (set by reset_state at the start of every piece of work)
-  f32x16 o[C::kDB];
-  float m_run;   // running max of c*log2e*s (lazy)
-  float negm;    // -m_run, or 0 while m_run is -inf
+  f32x16 o[NH][C::kDB];
+  float m_run[NH];   // running max of c*log2e*s (lazy)
+  float negm[NH];    // -m_run, or 0 while m_run is -inf
   // A block raises m_run when this lane's sum of its 16 probabilities exceeds
   // thr: 2^8 (probabilities are >= 0, so a sum <= 2^8 bounds each of them by
   // 2^8, and a probability above 2^8 makes the sum exceed it), or -1 while
   // m_run is -inf (every block raises until the row has a finite max).
-  float thr;
-  float l_run;   // row sum (this lane's half of the keys)
+  float thr[NH];
+  float l_run[NH];   // row sum (this lane's half of the keys)
+  // Two row halves (O in AGPRs, written by asm MFMAs whose latency the
+  // compiler cannot see): 24 wait states before VALU reads O (rescale,
+  // epilogue), tied to O so that no read of it moves above them; and 4 after
+  // VALU writes it (zeroing, rescale) before the next asm MFMA reads it.
+  static_assert(NH == 1 || C::kDB == 4, "two row halves at head_dim 128");
+  auto settle_o = [&](int rh) ULYS_INLINE {
+    if constexpr (NH == 2) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[rh][0]), "+a"(o[rh][1]), "+a"(o[rh][2]), "+a"(o[rh][3]));
+    }
+  };
+  auto settle_o_written = [&](int rh) ULYS_INLINE {
+    if constexpr (NH == 2) {
+      asm volatile("s_nop 3" : "+a"(o[rh][0]), "+a"(o[rh][1]), "+a"(o[rh][2]), "+a"(o[rh][3]));
+    }
+  };
   auto reset_state = [&]() {
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+    for (int rh = 0; rh < NH; ++rh) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    m_run = -INFINITY;
-    negm = 0.0f;
-    thr = -1.0f;
-    l_run = 0.0f;
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[rh][db][r] = 0.0f;
+      settle_o_written(rh);
+      m_run[rh] = -INFINITY;
+      negm[rh] = 0.0f;
+      thr[rh] = -1.0f;
+      l_run[rh] = 0.0f;
+    }
   };
 
   // Barrier publishing the next tile: this wave's loads of that tile have
@@ -339,7 +396,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // waves meet at s_barrier.  LDS reads still in flight are of stages in use
   // and may cross it.  The empty asm statements keep the compiler from moving
   // memory accesses across it.
-  constexpr int kInFlight = (kStages - 3) * C::kLoadsPerTile;
+  constexpr int kInFlight = (kStages - 3) * kLoadsPerTile;
   static_assert(kInFlight < 16, "vmcnt immediate");
   auto tile_barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | kInFlight);
@@ -393,38 +450,56 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < kKOffs; ++i) read_k_one(delta, kb, i, kf);
   };
 
-  // One head-dim step kk of S^T = K Q^T.
-  auto qk_step = [&](const KFrag& kf, int kk, f32x16 s) ULYS_INLINE {
-    if constexpr (!FP8) {
-      const u32x4 qx = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
+  // One head-dim step kk of S^T = K Q^T (row half rh).  Two row halves: an
+  // inline-asm MFMA reading Q from its AGPR tuple (a builtin would pull Q into
+  // VGPRs); the first step writes a fresh accumulator, early-clobbered so that
+  // it shares no register with the K operand.  Its result is read by VALU only
+  // after the wait states of the caller.
+  auto qk_step = [&](const KFrag& kf, int kk, f32x16 s, int rh) ULYS_INLINE {
+    if constexpr (NH == 2) {
+      const u32x4 qx = qa[rh][kk];
+      if (kk == 0)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(kf.x[kk]), "a"(qx));
+      else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf.x[kk]), "a"(qx));
+      return s;
+    } else if constexpr (!FP8) {
+      const u32x4 qx = {qf[rh][kk][0], qf[rh][kk][1], qf[rh][kk][2], qf[rh][kk][3]};
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[kk]),
                                                      __builtin_bit_cast(bf16x8, qx), s, 0, 0, 0);
     } else {
       const u32x4 k0x = kf.x[2 * kk], k1x = kf.x[2 * kk + 1];
       const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
                         (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
-      const i32x8 bq = {(int)qf[kk][0], (int)qf[kk][1], (int)qf[kk][2], (int)qf[kk][3],
-                        (int)qf[kk][4], (int)qf[kk][5], (int)qf[kk][6], (int)qf[kk][7]};
+      const i32x8 bq = {(int)qf[rh][kk][0], (int)qf[rh][kk][1], (int)qf[rh][kk][2], (int)qf[rh][kk][3],
+                        (int)qf[rh][kk][4], (int)qf[rh][kk][5], (int)qf[rh][kk][6], (int)qf[rh][kk][7]};
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s, 0, 0, 0, 127, 0, 127);
     }
   };
-  // S^T = K Q^T for one 32-key block.
-  auto qk = [&](const KFrag& kf) ULYS_INLINE {
+  // S^T = K Q^T for one 32-key block (row half rh).  Two row halves: 20 wait
+  // states before any VALU read of the scores.
+  auto qk = [&](const KFrag& kf, int rh) ULYS_INLINE {
     f32x16 s;
+    if constexpr (NH == 2) {
+#pragma unroll
+      for (int kk = 0; kk < C::kQKSteps; ++kk) s = qk_step(kf, kk, s, rh);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
+      return s;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < C::kQKSteps; ++kk) {
       if constexpr (!FP8) {
-        const u32x4 qx = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
+        const u32x4 qx = {qf[rh][kk][0], qf[rh][kk][1], qf[rh][kk][2], qf[rh][kk][3]};
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[kk]),
                                                     __builtin_bit_cast(bf16x8, qx), s, 0, 0, 0);
       } else {
         const u32x4 k0x = kf.x[2 * kk], k1x = kf.x[2 * kk + 1];
         const i32x8 af = {(int)k0x.x, (int)k0x.y, (int)k0x.z, (int)k0x.w,
                           (int)k1x.x, (int)k1x.y, (int)k1x.z, (int)k1x.w};
-        const i32x8 bq = {(int)qf[kk][0], (int)qf[kk][1], (int)qf[kk][2], (int)qf[kk][3],
-                          (int)qf[kk][4], (int)qf[kk][5], (int)qf[kk][6], (int)qf[kk][7]};
+        const i32x8 bq = {(int)qf[rh][kk][0], (int)qf[rh][kk][1], (int)qf[rh][kk][2], (int)qf[rh][kk][3],
+                          (int)qf[rh][kk][4], (int)qf[rh][kk][5], (int)qf[rh][kk][6], (int)qf[rh][kk][7]};
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bq, s, 0, 0, 0, 127, 0, 127);
       }
     }
@@ -449,12 +524,26 @@ void attn_fwd_kernel(AttnArgs a) {
       for (int e = 0; e < 2; ++e) read_v_one(vl, kb, db, e, vf);
   };
 
+  // One PV MFMA.  With two row halves O lives in AGPRs: the accumulate is
+  // written as inline asm with an AGPR accumulator (the VGPR form of the
+  // builtin would need all of O in VGPRs).  Its P operand is written by VALU at
+  // least 2 wait states earlier: a block before, or after the wait states that
+  // end the max-raise path and the piece set-up.
+  auto pv_one = [&](f32x16& acc, const bf16x8& va, const bf16x8& pb) ULYS_INLINE {
+    if constexpr (NH == 2) {
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(va), "v"(pb));
+    } else {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc, 0, 0, 0);
+    }
+  };
   // O^T += V^T P^T for one 32-key block.
-  auto pv = [&](const VFrag& vf, const bf16x8 (&p)[2]) ULYS_INLINE {
+  auto pv = [&](const VFrag& vf, const bf16x8 (&p)[NH][2]) ULYS_INLINE {
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.x[db][e], p[e], o[db], 0, 0, 0);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int rh = 0; rh < NH; ++rh) pv_one(o[rh][db], vf.x[db][e], p[rh][e]);
   };
 
   // Valid-key bits of the 32 keys from kb0 (bit j: key kb0 + j): inside
@@ -506,22 +595,20 @@ void attn_fwd_kernel(AttnArgs a) {
 
   // Probabilities exp2(c log2e s - m_run) of accumulator registers 8e..8e+7
   // -> bf16 B operand p[e] of the PV MFMA, and their fp32 sums in two chains.
-  auto probs_pair = [&](const f32x16& s, int e, int i, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
-    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, negm));
-    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, negm));
+  auto probs_pair = [&](const f32x16& s, int e, int i, bf16x8 (&p)[2], float& ls0, float& ls1, int rh) ULYS_INLINE {
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i], c2, negm[rh]));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * e + 2 * i + 1], c2, negm[rh]));
     const f32x2 xx = {x0, x1};
     const bf16x2 pk = __builtin_convertvector(xx, bf16x2);
     p[e][2 * i] = pk[0];
     p[e][2 * i + 1] = pk[1];
     if (e == 0 && i == 0) { ls0 = x0; ls1 = x1; } else { ls0 += x0; ls1 += x1; }
   };
-  auto probs_half = [&](const f32x16& s, int e, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
+  auto probs = [&](const f32x16& s, bf16x8 (&p)[2], float& ls0, float& ls1, int rh) ULYS_INLINE {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) probs_pair(s, e, i, p, ls0, ls1);
-  };
-  auto probs = [&](const f32x16& s, bf16x8 (&p)[2], float& ls0, float& ls1) ULYS_INLINE {
-    probs_half(s, 0, p, ls0, ls1);
-    probs_half(s, 1, p, ls0, ls1);
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) probs_pair(s, e, i, p, ls0, ls1, rh);
   };
 
   // The probabilities and sums are complete here (the empty asm consumes
@@ -538,23 +625,27 @@ void attn_fwd_kernel(AttnArgs a) {
   // recomputed from K in LDS, their max taken, and the probabilities redone
   // with the new max.
   auto raise_max = [&](int kdelta, int kb, int kb0, unsigned mword, bool dirty, bf16x8 (&p)[2], float& ls0,
-                       float& ls1) ULYS_INLINE {
+                       float& ls1, int rh) ULYS_INLINE {
     KFrag kf;
     read_k(kdelta, kb, kf);
-    f32x16 s = qk(kf);
+    f32x16 s = qk(kf, rh);
     mask(s, kb0, mword, dirty);
     const float mx = lane_swap_max(part_max(s)) * c2;
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
-    m_run = mn;
-    negm = (mn == -INFINITY) ? 0.0f : -mn;
-    thr = (mn == -INFINITY) ? -1.0f : kLazySum;
-    l_run *= alpha;
+    const float mn = fmaxf(m_run[rh], mx);
+    const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[rh] - mn);
+    m_run[rh] = mn;
+    negm[rh] = (mn == -INFINITY) ? 0.0f : -mn;
+    thr[rh] = (mn == -INFINITY) ? -1.0f : kLazySum;
+    l_run[rh] *= alpha;
+    settle_o(rh);
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    probs(s, p, ls0, ls1);
+      for (int r = 0; r < 16; ++r) o[rh][db][r] *= alpha;
+    settle_o_written(rh);
+    probs(s, p, ls0, ls1, rh);
+    // (two row halves: the new probabilities settle before an asm PV MFMA reads them)
+    if constexpr (NH == 2) asm volatile("s_nop 1" : "+v"(p[0]), "+v"(p[1]));
   };
 
   // ---- software pipeline over 32-key blocks ----
@@ -566,9 +657,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // tile is read from the iteration before its first block to its last block.
   // Scores and probabilities alternate between two register sets from one
   // block to the next (S(b) in one, S(b+1) in the other), so no copies.
-  f32x16 sA, sB;
+  f32x16 sA[NH], sB[NH];
   VFrag vf;
-  bf16x8 pA[2], pB[2];
+  bf16x8 pA[NH][2], pB[NH][2];
 
   constexpr int kPVMfma = 2 * C::kDB;
   constexpr int kQKMfma = C::kQKSteps;
@@ -576,54 +667,146 @@ void attn_fwd_kernel(AttnArgs a) {
   // Block b: s_in = S(b), p_in = P(b-1), vf = V(b-1) operands.  Produces
   // s_out = S(b+1) (K of stage st_next, block kb_next), p_out = P(b), and
   // vf = V(b) operands (stage st, block kb).  kb0 = first key of block b,
-  // mword = its key-mask word.
+  // mword = its key-mask word.  read_next(i, kf, part): part 0 reads K
+  // operand i of block b+1 into kf; part 1 is side work for the caller (only
+  // called with two row halves).
   auto iteration = [&](auto read_next, auto st, int kdelta, auto kb, int kb0, unsigned mword, bool dirty,
-                       f32x16& s_in, f32x16& s_out, bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) ULYS_INLINE {
-    mask(s_in, kb0, mword, dirty);
+                       f32x16 (&s_in)[NH], f32x16 (&s_out)[NH], bf16x8 (&p_in)[NH][2],
+                       bf16x8 (&p_out)[NH][2]) ULYS_INLINE {
+    // (two row halves: a dirty block masks its scores right away, so it first
+    // waits out the 12 wait states after the QK^T MFMAs that wrote them)
+    if constexpr (NH == 2) {
+      if (dirty) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s_in[0]), "+v"(s_in[1]));
+    }
+#pragma unroll
+    for (int rh = 0; rh < NH; ++rh) mask(s_in[rh], kb0, mword, dirty);
     KFrag kf;
-    float ls0, ls1;
+    float ls0[NH], ls1[NH];
+    f32x16 sn[NH];
+    if constexpr (NH == 2) {
+      // One wave per SIMD, so nothing else covers its stalls: both phases are
+      // placed by hand at one MFMA per issue group (the scheduler may not move
+      // work across a group boundary).  Beside each MFMA sits one step of the
+      // probability pipeline and at most one LDS read or tile load.
+      //
+      // The block's 32 probability elements per lane (element m: row half
+      // m % 2, score m / 2 of the PV phase's half of the keys, then of the QK^T
+      // phase's half) run through three stages, one group apart: scaled score
+      // (fma), exponential, then row sum and bf16 pack.  Stage r does the
+      // first of element r, the second of r-1 and the third of r-2; the 34
+      // stages are spread over the 32 groups (two in groups 14 and 29) so that
+      // the pipeline drains before the last MFMA instead of after it.  Each
+      // lane's two row sums add their elements in the same order as the
+      // two-wave shape, so the sums are bit-identical.
+      float tt[32], xx[32];
+      auto e_h = [](int m) { return m & 1; };
+      auto e_idx = [](int m) { return m < 16 ? (m >> 1) : 8 + ((m - 16) >> 1); };
+      auto stage = [&](int r) ULYS_INLINE {
+        if (r < 32) tt[r] = __builtin_fmaf(s_in[e_h(r)][e_idx(r)], c2, negm[e_h(r)]);
+        if (r >= 1 && r - 1 < 32) xx[r - 1] = __builtin_amdgcn_exp2f(tt[r - 1]);
+        if (r >= 2 && r - 2 < 32) {
+          const int m = r - 2, h = e_h(m), idx = e_idx(m);
+          const float x = xx[m];
+          if ((idx & 1) == 0) {
+            if (idx == 0) ls0[h] = x; else ls0[h] += x;
+          } else {
+            if (idx == 1) ls1[h] = x; else ls1[h] += x;
+            const f32x2 v2 = {xx[m - 2], x};
+            const bf16x2 pk = __builtin_convertvector(v2, bf16x2);
+            p_out[h][idx >> 3][(idx & 7) - 1] = pk[0];
+            p_out[h][idx >> 3][idx & 7] = pk[1];
+          }
+        }
+      };
+      // PV phase: group (g, rh) accumulates O[rh] over V fragment g; beside it
+      // the K read g of block b+1 (rh = 0) or the caller's side work (rh = 1,
+      // a clean step's tile load).
+#pragma unroll
+      for (int g = 0; g < kPVMfma; ++g) {
+        const int db = g % C::kDB, e = g / C::kDB;
+#pragma unroll
+        for (int rh = 0; rh < NH; ++rh) {
+          pv_one(o[rh][db], vf.x[db][e], p_in[rh][e]);
+          const int r = 2 * g + rh;   // 0..15
+          if (r < 14) stage(r); else if (r == 14) { stage(14); stage(15); } else stage(16);
+          read_next(g, kf, rh);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // QK^T phase: group (g, rh) is head-dim step g of S(b+1) for row half rh;
+      // beside the first of each pair, the V read g of block b.
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sn[rh][r] = 0.0f;
+#pragma unroll
+      for (int g = 0; g < kQKMfma; ++g) {
+#pragma unroll
+        for (int rh = 0; rh < NH; ++rh) {
+          sn[rh] = qk_step(kf, g, sn[rh], rh);
+          const int r = 16 + 2 * g + rh;   // 16..31
+          if (r < 29) stage(r + 1); else if (r == 29) { stage(30); stage(31); } else stage(r + 2);
+          if (rh == 0) read_v_one(v_of(st), kb, g % C::kDB, g / C::kDB, vf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
     // phase 1: PV(b-1) MFMAs in explicit issue groups (the scheduler may not
-    // move work across a group boundary), each MFMA with its share of the K
-    // reads of block b+1 and of the first half of the probabilities of block
-    // b beside it.
-    // Wave priority: high outside the QK^T phase's body, so that of the two
-    // waves on a SIMD the one issuing PV MFMAs and their K reads gets the issue
-    // slots while the other is inside its QK^T chain (measured +2-3%).
+    // move work across a group boundary), each V fragment feeding the MFMAs of
+    // every row half, with a share of the K reads of block b+1 and of the first
+    // half of the probabilities of block b beside them.
+    // Wave priority: high outside the QK^T phase's body.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < kPVMfma; ++g) {
       const int db = g % C::kDB, e = g / C::kDB;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.x[db][e], p_in[e], o[db], 0, 0, 0);
 #pragma unroll
-      for (int i = g * kKOffs / kPVMfma; i < (g + 1) * kKOffs / kPVMfma; ++i) read_next(i, kf);
+      for (int rh = 0; rh < NH; ++rh) pv_one(o[rh][db], vf.x[db][e], p_in[rh][e]);
 #pragma unroll
-      for (int i = g * 4 / kPVMfma; i < (g + 1) * 4 / kPVMfma; ++i) probs_pair(s_in, 0, i, p_out, ls0, ls1);
+      for (int i = g * kKOffs / kPVMfma; i < (g + 1) * kKOffs / kPVMfma; ++i) read_next(i, kf, 0);
+#pragma unroll
+      for (int j = g * 4 * NH / kPVMfma; j < (g + 1) * 4 * NH / kPVMfma; ++j)
+        probs_pair(s_in[j / 4], 0, j % 4, p_out[j / 4], ls0[j / 4], ls1[j / 4], j / 4);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // phase 2: QK(b+1) MFMAs, the V reads of block b (into the registers
-    // PV(b-1) consumed) and the second half of the probabilities, in the same
-    // shares as a hint but ordered by the scheduler (measured faster than
-    // pinned groups here: it issues the exponentials early and the V reads
-    // late)
+    // phase 2: QK(b+1) MFMAs (each K fragment feeding every row half), the V
+    // reads of block b and the second half of the probabilities, ordered by
+    // the scheduler
     __builtin_amdgcn_s_setprio(0);
-    f32x16 sn;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sn[r] = 0.0f;
+    for (int rh = 0; rh < NH; ++rh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[rh][r] = 0.0f;
 #pragma unroll
     for (int g = 0; g < kQKMfma; ++g) {
-      sn = qk_step(kf, g, sn);
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh) sn[rh] = qk_step(kf, g, sn[rh], rh);
 #pragma unroll
       for (int j = g * (2 * C::kDB) / kQKMfma; j < (g + 1) * (2 * C::kDB) / kQKMfma; ++j)
         read_v_one(v_of(st), kb, j % C::kDB, j / C::kDB, vf);
 #pragma unroll
-      for (int i = g * 4 / kQKMfma; i < (g + 1) * 4 / kQKMfma; ++i) probs_pair(s_in, 1, i, p_out, ls0, ls1);
+      for (int j = g * 4 * NH / kQKMfma; j < (g + 1) * 4 * NH / kQKMfma; ++j)
+        probs_pair(s_in[j / 4], 1, j % 4, p_out[j / 4], ls0[j / 4], ls1[j / 4], j / 4);
     }
+    }
+    // (two row halves: S(b+1) is read by VALU no sooner than the next block's
+    // second probability stage, at least 12 wait states on, or after the wait
+    // states a dirty block takes first)
+    if constexpr (NH == 2) asm volatile("" : "+v"(sn[0]), "+v"(sn[1]));
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
-    s_out = sn;
-    pin(p_out, ls0, ls1);
-    if (__any(ls0 + ls1 > thr)) raise_max(kdelta, kb, kb0, mword, dirty, p_out, ls0, ls1);
-    l_run += ls0 + ls1;
+    if constexpr (NH == 1) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int rh = 0; rh < NH; ++rh) {
+      s_out[rh] = sn[rh];
+      pin(p_out[rh], ls0[rh], ls1[rh]);
+    }
+#pragma unroll
+    for (int rh = 0; rh < NH; ++rh) {
+      const bool raise = __any(ls0[rh] + ls1[rh] > thr[rh]);
+      if (NH == 2 ? __builtin_expect(raise, 0) : raise)   // (one wave per SIMD: the rare path out of line)
+        raise_max(kdelta, kb, kb0, mword, dirty, p_out[rh], ls0[rh], ls1[rh], rh);
+      l_run[rh] += ls0[rh] + ls1[rh];
+    }
   };
 
   using B0 = std::integral_constant<int, 0>;
@@ -635,7 +818,7 @@ void attn_fwd_kernel(AttnArgs a) {
   const int nskip = max(0, skip_last - skip_first);
   int nseq = ntiles - nskip;
   if constexpr (MASK) {
-    const int per = (ntiles + kThreads - 1) / kThreads;
+    const int per = (ntiles + kT - 1) / kT;
     const int t0 = min(tid * per, ntiles), t1 = min(t0 + per, ntiles);
     int cnt = 0;
     for (int t = t0; t < t1; ++t)   // (each thread its own tiles: lane-local bits)
@@ -643,14 +826,14 @@ void attn_fwd_kernel(AttnArgs a) {
     int* scan = (int*)lds;   // the ring is not in use yet
     scan[tid] = cnt;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < kT; off <<= 1) {
       const int add = tid >= off ? scan[tid - off] : 0;
       __syncthreads();
       scan[tid] += add;
       __syncthreads();
     }
     int pos = scan[tid] - cnt;
-    nseq = scan[kThreads - 1];
+    nseq = scan[kT - 1];
     for (int t = t0; t < t1; ++t)
       if ((valid_bits(t * kBN, mask_word(t * kBN)) | valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) != 0u)
         tile_list[pos++] = (unsigned short)t;
@@ -702,13 +885,17 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     const long long upiece = (long long)qtile * nunits + p0;
     u = ranged ? upiece + max(n, 1) : uend;
-    const int qrow0 = qtile * kBM + wave * 32;
+    const int qrow0 = qtile * kBM + wave * 32 * NH;
     load_q(qrow0);
     reset_state();
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pA[e][i] = (__bf16)0.0f;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pA[rh][e][i] = (__bf16)0.0f;
+    // (two row halves: the zeros settle before the first asm PV MFMA reads them)
+    if constexpr (NH == 2) asm volatile("s_nop 1" : "+v"(pA[0][0]), "+v"(pA[0][1]), "+v"(pA[1][0]), "+v"(pA[1][1]));
 
     // (uniform across the workgroup: kept in scalar registers)
     auto seq_tile = [&](int pos) {
@@ -731,7 +918,8 @@ void attn_fwd_kernel(AttnArgs a) {
       {
         KFrag kf;
         read_k(-C::kKTile, B0{}, kf);
-        sA = qk(kf);
+#pragma unroll
+        for (int rh = 0; rh < NH; ++rh) sA[rh] = qk(kf, rh);
         read_v(v_of(B0{}), B0{}, vf);   // finite operands for the empty PV of block -1
       }
       int tc = seq_tile(0);
@@ -749,7 +937,7 @@ void attn_fwd_kernel(AttnArgs a) {
       // mask words of the tile's second block (mw1) and of the next tile's blocks
       // (fetched a block ahead: each is a scalar value once it is used)
       unsigned mw1 = mask_word(tc * kBN + 32);
-      iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
+      iteration([&](int i, KFrag& kf, int part) ULYS_INLINE { if (part == 0) read_k_one(-C::kKTile, B1{}, i, kf); }, B0{}, -C::kKTile, B0{},
                 tc * kBN,
                 __builtin_amdgcn_readfirstlane(mask_word(tc * kBN)), dc, sA, sB, pA, pB);
       tile_barrier();
@@ -763,14 +951,14 @@ void attn_fwd_kernel(AttnArgs a) {
         load_pos(i + kStages - 1, SP);
         const int tn = i + 1 < n ? seq_tile(i + 1) : tc;
         const unsigned wn0 = mask_word(tn * kBN), wn1 = mask_word(tn * kBN + 32);
-        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
+        iteration([&](int i, KFrag& kf, int part) ULYS_INLINE { if (part == 0) read_k_one(0, B0{}, i, kf); }, SA, (int(SA) - int(SB)) * C::kKTile, B1{},
                   tc * kBN + 32,
                   __builtin_amdgcn_readfirstlane(mw1), dc, sB, sA, pB, pA);
         if (i + 1 >= n) return false;
         tc = tn;
         mw1 = wn1;
         dc = is_dirty(tc);
-        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
+        iteration([&](int i, KFrag& kf, int part) ULYS_INLINE { if (part == 0) read_k_one(0, B1{}, i, kf); }, SB, 0, B0{}, tc * kBN,
                   __builtin_amdgcn_readfirstlane(wn0), dc, sA, sB, pA, pB);
         // the next step reads K from the stage after SB
         const int adv = int(SB) == kStages - 1 ? -(kStages - 1) * C::kKTile : C::kKTile;
@@ -795,17 +983,32 @@ void attn_fwd_kernel(AttnArgs a) {
       auto clean_step = [&](auto SA, auto SB, auto SP) ULYS_INLINE {
         const unsigned int kl = lds_u32(k_of(SP)) + kls;
         const unsigned int vl = lds_u32(v_of(SP) + kVRegion) + vls;
-#pragma unroll
-        for (int u = 0; u < C::kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kWaves * 1024);
-#pragma unroll
-        for (int u = 0; u < C::kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kWaves * 1024);
-        ktp += ktile;
-        vtp += vtile;
         const int ka = int(SA) * C::kKTile, kbb = int(SB) * C::kKTile;
-        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B0{}, i, kf); }, SA, ka, B1{}, 0, ~0u,
-                  false, sB, sA, pB, pA);
-        iteration([&](int i, KFrag& kf) ULYS_INLINE { read_k_one(kbb, B1{}, i, kf); }, SB, kbb, B0{}, 0, ~0u,
-                  false, sA, sB, pA, pB);
+        // With one wave per SIMD a burst of tile loads would stall the wave's
+        // MFMAs: its eight loads go one each beside the second row half's PV
+        // MFMAs of the step's first block instead.
+        constexpr bool kSpread = NH == 2;
+        static_assert(!kSpread || kKSegsPerWave + kVSegsPerWave == kKOffs, "one tile load per PV group");
+        if constexpr (kSpread) {
+          iteration([&](int i, KFrag& kf, int part) ULYS_INLINE {
+                      if (part == 0) { read_k_one(kbb, B0{}, i, kf); return; }
+                      if (i < kKSegsPerWave) dma16(ktp, kgo_u[i], kl + i * kW * 1024);
+                      else dma16(vtp, vgo_u[i - kKSegsPerWave], vl + (i - kKSegsPerWave) * kW * 1024);
+                    }, SA, ka, B1{}, 0, ~0u, false, sB, sA, pB, pA);
+          ktp += ktile;
+          vtp += vtile;
+        } else {
+#pragma unroll
+          for (int u = 0; u < kKSegsPerWave; ++u) dma16(ktp, kgo_u[u], kl + u * kW * 1024);
+#pragma unroll
+          for (int u = 0; u < kVSegsPerWave; ++u) dma16(vtp, vgo_u[u], vl + u * kW * 1024);
+          ktp += ktile;
+          vtp += vtile;
+          iteration([&](int i, KFrag& kf, int part) ULYS_INLINE { if (part == 0) read_k_one(kbb, B0{}, i, kf); },
+                    SA, ka, B1{}, 0, ~0u, false, sB, sA, pB, pA);
+        }
+        iteration([&](int i, KFrag& kf, int part) ULYS_INLINE { if (part == 0) read_k_one(kbb, B1{}, i, kf); },
+                  SB, kbb, B0{}, 0, ~0u, false, sA, sB, pA, pB);
         tile_barrier();
       };
       // Clean steps from step i: the first tile at or after step i's that is
@@ -870,8 +1073,11 @@ void attn_fwd_kernel(AttnArgs a) {
     // (a key-range chunk, or a range's piece of a tile it shares with other
     // ranges: o in fp32 and lse in the log2 domain, to be merged)
     const int ft = fresh_tid();
-    const int row = qrow0 + (ft & 31), hh = (ft >> 5) & 1, l32 = ft & 31;
-    const float l = lane_swap_sum(l_run);
+#pragma unroll
+    for (int rh = 0; rh < NH; ++rh) {
+    settle_o(rh);
+    const int row = qrow0 + rh * 32 + (ft & 31), hh = (ft >> 5) & 1, l32 = ft & 31;
+    const float l = lane_swap_sum(l_run[rh]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const bool whole = !ranged || (p0 == 0 && n == nseq);
     if (!ranged && a.splits > 1) {
@@ -882,13 +1088,13 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                              o[db][4 * r4 + 3] * inv};
+            const f32x4 w = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv, o[rh][db][4 * r4 + 2] * inv,
+                              o[rh][db][4 * r4 + 3] * inv};
             *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
           }
         if (hh == 0)
           a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] =
-              l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+              l > 0.0f ? m_run[rh] + __log2f(l) : -INFINITY;
       }
     } else if (whole) {
       if (row < qrows) {
@@ -897,8 +1103,8 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x2 lo = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv};
-            const f32x2 hi = {o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
+            const f32x2 lo = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv};
+            const f32x2 hi = {o[rh][db][4 * r4 + 2] * inv, o[rh][db][4 * r4 + 3] * inv};
             const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
             const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
             u32x2 w;
@@ -907,7 +1113,7 @@ void attn_fwd_kernel(AttnArgs a) {
             *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
           }
         if (a.lse != nullptr && hh == 0)
-          a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+          a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run[rh] + __log2f(l)) * kLn2 : -INFINITY;
       }
     } else {
       // A piece of a tile shared with neighbouring ranges (merged by
@@ -916,17 +1122,18 @@ void attn_fwd_kernel(AttnArgs a) {
       const int slot = upiece == ustart ? 0 : 1;
       const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + wx) * 2 + slot;
       if (row < qrows) {
-        float* pp = a.part_o + (pidx * kBM + wave * 32 + l32) * D;
+        float* pp = a.part_o + (pidx * kBM + wave * 32 * NH + rh * 32 + l32) * D;
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 w = {o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
-                              o[db][4 * r4 + 3] * inv};
+            const f32x4 w = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv, o[rh][db][4 * r4 + 2] * inv,
+                              o[rh][db][4 * r4 + 3] * inv};
             *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
           }
-        if (hh == 0) a.part_lse[pidx * kBM + wave * 32 + l32] = l > 0.0f ? m_run + __log2f(l) : -INFINITY;
+        if (hh == 0) a.part_lse[pidx * kBM + wave * 32 * NH + rh * 32 + l32] = l > 0.0f ? m_run[rh] + __log2f(l) : -INFINITY;
       }
+    }
     }
     if (u < uend || tail_u >= 0) {
       // the next piece refills the ring: every tile load of this one has
@@ -1088,10 +1295,11 @@ __global__ __launch_bounds__(kThreads) void range_merge_kernel(AttnArgs a) {
 template <int D, bool FP8>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.ranges > 0 ? a.ranges : a.qtiles * a.splits, a.hsub, a.batch);
+  constexpr int kNHm = kRowHalves<D, FP8, true>, kNH = kRowHalves<D, FP8, false>;
   if (a.key_mask != nullptr)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, true, kNHm>), grid, dim3(kThreads / kNHm), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, false>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, false, kNH>), grid, dim3(kThreads / kNH), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ranges > 0) {
