@@ -530,7 +530,7 @@ def summarize_profiles(d: str):
                       f"{ar:.4g} / {aw:.4g} | {k[RD] * 32 / ar:.3f} | {k[WR] * 32 / aw:.3f} |")
     print("\n## MFMA utilisation of the attention kernel (SQ counters)\n")
     print("| G | kernel us | GRBM_GUI_ACTIVE / XCD | clock GHz | MFMA busy (of SIMD-cycles) | MFMA FLOPs / algorithmic | "
-          "VALU / 32-key block / wave | SALU / block | LDS / block | LDS bank conflicts |")
+          "VALU per 32 rows x 32 keys | SALU per 32 x 32 | LDS per 32 x 32 | LDS bank conflicts |")
     print("|---|---|---|---|---|---|---|---|---|---|")
     for G in (1, 5):
         heads = 10 // G
@@ -540,7 +540,7 @@ def summarize_profiles(d: str):
         busy = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024)
         flops = a["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         alg = 4.0 * rows * rows * 128 * heads
-        blocks = heads * (rows / 32) * (rows / 32)      # (32-row wave, 32-key block) pairs
+        blocks = heads * (rows / 32) * (rows / 32)      # (32 query rows, 32-key block) pairs
         mfma_insts = flops / (32 * 32 * 16 * 2)
         out["per_groups"][str(G)]["mfma"] = {"kernel_us": round(a["dur_ns"] / 1e3, 1), "clock_ghz": round(ghz, 3),
                                              "mfma_busy_frac": round(busy, 4),
