@@ -789,9 +789,10 @@ void attn_fwd_kernel(AttnArgs a) {
         probs_pair(s_in[j / 4], 1, j % 4, p_out[j / 4], ls0[j / 4], ls1[j / 4], j / 4);
     }
     }
-    // (two row halves: S(b+1) is read by VALU no sooner than the next block's
-    // second probability stage, at least 12 wait states on, or after the wait
-    // states a dirty block takes first)
+    // (two row halves: no wait states here.  S(b+1) is first read by VALU in
+    // the next block's first probability step, which comes after this block's
+    // max checks and the next block's first PV MFMA, more than 12 wait states
+    // on; a dirty block, which masks its scores first, waits at its start)
     if constexpr (NH == 2) asm volatile("" : "+v"(sn[0]), "+v"(sn[1]));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NH == 1) __builtin_amdgcn_s_setprio(1);
