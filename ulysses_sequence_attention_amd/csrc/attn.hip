@@ -182,6 +182,10 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * (C::kKTile + C::kVTile)];
   // Tiles with at least one valid key, in order, when a key mask is given.
   __shared__ unsigned short tile_list[kMaxMaskTiles];
+  // Per-wave staging of the output rows (128 bytes of each row at a time, rows
+  // 144 bytes apart): global stores then write whole lines.
+  constexpr int kStgPitch = 144;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[kWaves * 32 * kStgPitch];
   // Stage st's K tile; its V tile sits at v_of(st) + the V region offset, which
   // the per-lane V read offsets carry (so every LDS read's immediate offset
   // stays below 64 KB).
@@ -1073,68 +1077,90 @@ void attn_fwd_kernel(AttnArgs a) {
     // ---- epilogue: normalise, write o (bf16) and lse (fp32, natural log) ----
     // (a key-range chunk, or a range's piece of a tile it shares with other
     // ranges: o in fp32 and lse in the log2 domain, to be merged)
+    // The rows leave through this wave's LDS staging area, 128 bytes of each
+    // row at a time: a global store then covers whole 128-byte lines (8 lanes
+    // per line) instead of 16 bytes of 32 different rows.
     const int ft = fresh_tid();
+    const int l32f = ft & 31, hhf = (ft >> 5) & 1, lanef = ft & 63;
+    // (written directly: a whole tile; else fp32 partials to be merged)
+    const bool whole = ranged ? (p0 == 0 && n == nseq) : a.splits <= 1;
+    constexpr int kRW = 32 * NH;   // rows of this wave
+    unsigned char* const stg = stage_lds + wave * kRW * kStgPitch;
+    float inv[NH], lse2[NH];
 #pragma unroll
     for (int rh = 0; rh < NH; ++rh) {
-    settle_o(rh);
-    const int row = qrow0 + rh * 32 + (ft & 31), hh = (ft >> 5) & 1, l32 = ft & 31;
-    const float l = lane_swap_sum(l_run[rh]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const bool whole = !ranged || (p0 == 0 && n == nseq);
-    if (!ranged && a.splits > 1) {
-      if (row < qrows) {
-        const size_t prow = ((size_t)split * a.batch + b) * qrows + row;
-        float* pp = a.part_o + (prow * a.hsub + hl) * D;
+      settle_o(rh);
+      const float l = lane_swap_sum(l_run[rh]);
+      inv[rh] = l > 0.0f ? 1.0f / l : 0.0f;
+      lse2[rh] = l > 0.0f ? m_run[rh] + __log2f(l) : -INFINITY;
+    }
+    if (whole) {
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db)
+      for (int c = 0; c < D / 64; ++c) {   // head dims [64c, 64c + 64): 128 bytes of bf16
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 w = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv, o[rh][db][4 * r4 + 2] * inv,
-                              o[rh][db][4 * r4 + 3] * inv};
-            *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
-          }
-        if (hh == 0)
-          a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] =
-              l > 0.0f ? m_run[rh] + __log2f(l) : -INFINITY;
+        for (int rh = 0; rh < NH; ++rh)
+#pragma unroll
+          for (int dbi = 0; dbi < 2; ++dbi)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int db = 2 * c + dbi;
+              const f32x2 lo = {o[rh][db][4 * r4 + 0] * inv[rh], o[rh][db][4 * r4 + 1] * inv[rh]};
+              const f32x2 hi = {o[rh][db][4 * r4 + 2] * inv[rh], o[rh][db][4 * r4 + 3] * inv[rh]};
+              u32x2 w;
+              w.x = __builtin_bit_cast(unsigned int, __builtin_convertvector(lo, bf16x2));
+              w.y = __builtin_bit_cast(unsigned int, __builtin_convertvector(hi, bf16x2));
+              *(u32x2*)(stg + (rh * 32 + l32f) * kStgPitch + (dbi * 32 + 8 * r4 + 4 * hhf) * 2) = w;
+            }
+#pragma unroll
+        for (int kq = 0; kq < kRW / 8; ++kq) {
+          const int lr = kq * 8 + (lanef >> 3), ch = lanef & 7;
+          const u32x4 x = *(const u32x4*)(stg + lr * kStgPitch + ch * 16);
+          const int row = qrow0 + lr;
+          if (row < qrows)
+            *(u32x4*)(a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D + c * 64 + ch * 8) = x;
+        }
       }
-    } else if (whole) {
-      if (row < qrows) {
-        uint16_t* op = a.o + ((size_t)b * qrows + row) * q_row_stride + (size_t)head * D;
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x2 lo = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv};
-            const f32x2 hi = {o[rh][db][4 * r4 + 2] * inv, o[rh][db][4 * r4 + 3] * inv};
-            const bf16x2 blo = __builtin_convertvector(lo, bf16x2);
-            const bf16x2 bhi = __builtin_convertvector(hi, bf16x2);
-            u32x2 w;
-            w.x = __builtin_bit_cast(unsigned int, blo);
-            w.y = __builtin_bit_cast(unsigned int, bhi);
-            *(u32x2*)(op + db * 32 + 8 * r4 + 4 * hh) = w;
-          }
-        if (a.lse != nullptr && hh == 0)
-          a.lse[((size_t)b * a.hq + head) * qrows + row] = l > 0.0f ? (m_run[rh] + __log2f(l)) * kLn2 : -INFINITY;
+      for (int rh = 0; rh < NH; ++rh) {
+        const int row = qrow0 + rh * 32 + l32f;
+        if (a.lse != nullptr && hhf == 0 && row < qrows)
+          a.lse[((size_t)b * a.hq + head) * qrows + row] = lse2[rh] * kLn2;
       }
     } else {
-      // A piece of a tile shared with neighbouring ranges (merged by
-      // range_merge_kernel): slot 0 if it is this range's first piece, 1 if
-      // its last.
-      const int slot = upiece == ustart ? 0 : 1;
-      const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + wx) * 2 + slot;
-      if (row < qrows) {
-        float* pp = a.part_o + (pidx * kBM + wave * 32 * NH + rh * 32 + l32) * D;
+      // fp32 rows: a key-range chunk's at its (split, b, row, head) position, a
+      // cut tile's piece in slot 0 (the range's first piece) or 1 (its last)
+      const bool keysplit = !ranged;
+      const size_t pidx = (((size_t)b * a.hsub + hl) * a.ranges + wx) * 2 + (upiece == ustart ? 0 : 1);
+      auto prow = [&](int row) -> float* {
+        if (keysplit) return a.part_o + ((((size_t)split * a.batch + b) * qrows + row) * a.hsub + hl) * D;
+        return a.part_o + (pidx * kBM + (row - qtile * kBM)) * D;
+      };
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db)
+      for (int c = 0; c < D / 32; ++c) {   // head dims [32c, 32c + 32): 128 bytes of fp32
+#pragma unroll
+        for (int rh = 0; rh < NH; ++rh)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 w = {o[rh][db][4 * r4 + 0] * inv, o[rh][db][4 * r4 + 1] * inv, o[rh][db][4 * r4 + 2] * inv,
-                              o[rh][db][4 * r4 + 3] * inv};
-            *(f32x4*)(pp + db * 32 + 8 * r4 + 4 * hh) = w;
+            const f32x4 w = {o[rh][c][4 * r4 + 0] * inv[rh], o[rh][c][4 * r4 + 1] * inv[rh],
+                              o[rh][c][4 * r4 + 2] * inv[rh], o[rh][c][4 * r4 + 3] * inv[rh]};
+            *(f32x4*)(stg + (rh * 32 + l32f) * kStgPitch + (8 * r4 + 4 * hhf) * 4) = w;
           }
-        if (hh == 0) a.part_lse[pidx * kBM + wave * 32 * NH + rh * 32 + l32] = l > 0.0f ? m_run[rh] + __log2f(l) : -INFINITY;
+#pragma unroll
+        for (int kq = 0; kq < kRW / 8; ++kq) {
+          const int lr = kq * 8 + (lanef >> 3), ch = lanef & 7;
+          const f32x4 x = *(const f32x4*)(stg + lr * kStgPitch + ch * 16);
+          const int row = qrow0 + lr;
+          if (row < qrows) *(f32x4*)(prow(row) + c * 32 + ch * 4) = x;
+        }
       }
-    }
+#pragma unroll
+      for (int rh = 0; rh < NH; ++rh) {
+        const int row = qrow0 + rh * 32 + l32f;
+        if (hhf == 0 && row < qrows) {
+          if (keysplit) a.part_lse[(((size_t)split * a.batch + b) * a.hsub + hl) * qrows + row] = lse2[rh];
+          else a.part_lse[pidx * kBM + (row - qtile * kBM)] = lse2[rh];
+        }
+      }
     }
     if (u < uend || tail_u >= 0) {
       // the next piece refills the ring: every tile load of this one has
