@@ -72,6 +72,9 @@
 //    run of its (b, h)'s (query tile, key tile) sequence, walked as pieces.
 //    A tile computed in parts leaves fp32 partials (o, lse) that a second
 //    kernel merges in a fixed order (split_merge_kernel, range_merge_kernel).
+//  * Output rows (bf16, or the fp32 partials) leave through a per-wave LDS
+//    staging area, 128 bytes of each row at a time, so that every global
+//    store writes whole 128-byte lines.
 // A head's arithmetic never depends on the other heads of the call, the grid
 // or the slot strides, so a head-group split reproduces the full call's bytes.
 #include <algorithm>
