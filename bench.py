@@ -140,9 +140,10 @@ class RankStep:
     """One simulated rank's path on a layout: [amax] -> pack (all groups) -> G attention calls -> unpack,
     with two rotating slot sets and one workspace, all allocated once."""
 
-    def __init__(self, torch, ulys, L, shards, key_gaps=None, fp8=False, amax_each_step=False):
+    def __init__(self, torch, ulys, L, shards, key_gaps=None, fp8=False, amax_each_step=False, key_mask=None):
         self.torch, self.ulys, self.L = torch, ulys, L
         self.shards, self.gaps, self.fp8, self.amax_each_step = shards, key_gaps, fp8, amax_each_step
+        self.key_mask = key_mask
         dev = shards["q"][0].device
         G, B = L.groups, L.batch
         qk_dtype = torch.uint8 if fp8 else torch.bfloat16
@@ -179,8 +180,13 @@ class RankStep:
                     qk_dtype=self.qk, qk_amax=self.amax if self.fp8 else None)
         mark(j); j += 1
         for g in range(L.groups):
-            u.ulys_attend_group(s["q"][g], s["k"][g], s["v"][g], s["o"][g], s["lse"][g], key_gaps=self.gaps,
-                                qk_dtype=self.qk, qk_amax=self.amax if self.fp8 else None, workspace=self.ws)
+            if self.key_mask is None:
+                u.ulys_attend_group(s["q"][g], s["k"][g], s["v"][g], s["o"][g], s["lse"][g], key_gaps=self.gaps,
+                                    qk_dtype=self.qk, qk_amax=self.amax if self.fp8 else None, workspace=self.ws)
+            else:
+                u.ulys_attend_group_ex(s["q"][g], s["k"][g], s["v"][g], s["o"][g], s["lse"][g],
+                                       key_gaps=self.gaps, key_mask=self.key_mask, qk_dtype=self.qk,
+                                       qk_amax=self.amax if self.fp8 else None, workspace=self.ws)
         mark(j); j += 1
         u.ulys_unpack(L, rank, -1, s["o"], self.out)
         mark(j)
@@ -206,7 +212,9 @@ def shards_of(torch, inputs, w, dev):
     P, S_l, R = w.degree, w.s_local, w.n_rep
     out = {}
     for name, x in (("q", q), ("k", k), ("v", v)):
-        if R == 0:
+        if R > 0 and name == "q" and w.extra.get("kv_only_prefix"):   # the prefix is k/v only
+            out[name] = [x[:, R + p * S_l:R + (p + 1) * S_l].contiguous().to(dev) for p in range(P)]
+        elif R == 0:
             out[name] = [x[:, p * S_l:(p + 1) * S_l].contiguous().to(dev) for p in range(P)]
         else:                       # a replicated prefix: every shard carries it in front
             out[name] = [torch.cat([x[:, :R], x[:, R + p * S_l:R + (p + 1) * S_l]], dim=1).contiguous().to(dev)
@@ -224,9 +232,9 @@ def input_sha256(torch, tensors) -> str:
 
 
 def run_config(torch, ulys, args, stream, L, shards, flops_step, peak, kernel, gaps=None, fp8=False,
-               amax_each_step=False, traffic=None, extra=None):
+               amax_each_step=False, traffic=None, extra=None, key_mask=None):
     """Time RankStep over the config; returns the JSON object for it (attention roofline included)."""
-    st = RankStep(torch, ulys, L, shards, gaps, fp8, amax_each_step)
+    st = RankStep(torch, ulys, L, shards, gaps, fp8, amax_each_step, key_mask)
     ms, per_step, seg = time_steps(torch, stream, st, st.segments(), args.warmup, args.steps)
     launch_ms = sum(seg["attend"]) / len(seg["attend"]) / L.groups
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -664,6 +672,29 @@ def main():
             del stw, sh
             torch.cuda.empty_cache()
             print(json.dumps({"progress": name}), file=sys.stderr, flush=True)
+        # cross-attention to a replicated text K/V prefix with its padding as a key mask (valid-key FLOPs)
+        import numpy as np
+        wk = inputs.KV_PREFIX_MASKED
+        _, sh = shards_of(torch, inputs, wk, dev)
+        Lw = ulys.Layout(wk.batch, wk.degree, wk.s_local, wk.n_rep, ulys.ULYS_REP_KV_PREFIX, wk.hq, wk.hkv,
+                         wk.head_dim, wk.groups)
+        valid_mask = np.ones((wk.batch, Lw.rows), dtype=bool)
+        valid_mask[:, wk.extra["text_valid"]:wk.n_rep] = False
+        words = inputs.key_mask_words(valid_mask).to(dev)
+        valid = int(valid_mask.sum()) // wk.batch
+        fl = 4.0 * wk.batch * (wk.hq // wk.degree) * Lw.rows_q * valid * wk.head_dim
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        r, stw = run_config(torch, ulys, args, stream, Lw, sh, fl, PEAK_BF16_TFLOPS,
+                            "attn_fwd_kernel<128, false, true, 1>" + (f" + {MERGE_KERNEL}" if ulys.ulys_attend_ranges(
+                                Lw.batch, Lw.rows_q, Lw.rows, cus) else ""),
+                            key_mask=words,
+                            extra={"flops_per_step": fl, "q_rows": Lw.rows_q, "kv_rows": Lw.rows, "valid_keys": valid,
+                                   "note": "K/V-only text prefix (512 rows, 226 valid) replicated on the 4 ranks, "
+                                           "padding as a key-mask bit array; q and o hold only the image rows"})
+        configs["kv_prefix_masked"] = r
+        del stw, sh
+        torch.cuda.empty_cache()
+        print(json.dumps({"progress": "kv_prefix_masked"}), file=sys.stderr, flush=True)
         res["configs"] = configs
         res["repack"]["fp8_pack_gbs"] = configs["e2e_p4_fp8_step"]["pack_gbs"]
         res["repack"]["amax_gbs"] = configs["e2e_p4_fp8_step"]["amax_gbs"]

@@ -302,3 +302,38 @@ def test_mask_bits_past_the_last_key_are_ignored(gpu, splits):
     torch.cuda.synchronize()
     o_ref, l_ref = oatt.attention(_as_f64(q), _as_f64(k), _as_f64(v), oatt.default_scale(d), gaps, key_mask=m)
     check_attention(o, l, o_ref, l_ref, label=f"mask bits past the end, splits {splits}")
+
+
+def test_kv_prefix_masked_wan_share_full_size(gpu):
+    """The bench's K/V-only-prefix workload at full size: four ranks' q shards hold only their 6820 image
+    rows; the k/v shards carry 512 replicated text rows in front, of which the first 226 are valid by a
+    key-mask bit array.  For rank 1, group 2 (2 of its 10 heads): the library's pack equals the oracle's
+    K/V-prefix pack byte for byte; attention with the mask equals the same call with the padding given as
+    a key gap byte for byte (o and lse); sampled rows match the oracle with the mask."""
+    w = inputs.KV_PREFIX_MASKED
+    q, k, v = inputs.global_qkv(w)
+    P, S_l, R, G = w.degree, w.s_local, w.n_rep, w.groups
+    qs = [bits(q[:, R + p * S_l:R + (p + 1) * S_l]) for p in range(P)]
+    ks = [np.concatenate([bits(k[:, :R]), bits(k[:, R + p * S_l:R + (p + 1) * S_l])], axis=1) for p in range(P)]
+    vs = [np.concatenate([bits(v[:, :R]), bits(v[:, R + p * S_l:R + (p + 1) * S_l])], axis=1) for p in range(P)]
+    L = gpu.Layout(w.batch, P, S_l, R, gpu.ULYS_REP_KV_PREFIX, w.hq, w.hkv, w.head_dim, G)
+    rank, g = 1, 2
+    print(f"kv prefix masked: q rows {L.rows_q}, kv rows {L.rows}, rank {rank} group {g}", flush=True)
+    dq = torch.empty((w.batch, L.rows_q, L.gq, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty((w.batch, L.rows, L.gkv, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    gpu.ulys_pack(L, rank, g, [from_bits(x) for x in qs], [from_bits(x) for x in ks], [from_bits(x) for x in vs],
+                  dq, dk, dv)
+    torch.cuda.synchronize()
+    rq, rk, rv = olay.pack_kv_prefix(qs, ks, vs, rank, g, G, R)
+    assert np.array_equal(bits(dq), rq) and np.array_equal(bits(dk), rk) and np.array_equal(bits(dv), rv)
+    mask = np.ones((w.batch, L.rows), dtype=bool)
+    mask[:, w.extra["text_valid"]:R] = False
+    om, lm = _attend_ex(gpu, dq, dk, dv, mask=mask)
+    og, lg = _attend_ex(gpu, dq, dk, dv, gaps=[(w.extra["text_valid"], R)] * w.batch)
+    assert np.array_equal(bits(om), bits(og)), "o: mask path differs from gap path"
+    assert np.array_equal(lm.cpu().numpy().view(np.int32), lg.cpu().numpy().view(np.int32)), "lse differs"
+    rows = sample_rows(L.rows_q, boundaries=(S_l, 2 * S_l, 3 * S_l), edge=4, extra=24)
+    o_ref, l_ref = oatt.attention(_as_f64(rq), _as_f64(rk), _as_f64(rv), oatt.default_scale(w.head_dim),
+                                  rows=rows, key_mask=mask)
+    check_attention(om, lm, o_ref, l_ref, rows=rows, label="kv prefix masked, Wan share")

@@ -53,8 +53,13 @@ GQA = Workload("gqa", 4, batch=2, degree=1, s_local=16384, n_rep=0, rep_first=Tr
                hq=16, hkv=4, head_dim=128, groups=4, q_mult=2.0)
 E2E_P4 = Workload("e2e_p4", 5, batch=1, degree=4, s_local=6820, n_rep=0, rep_first=True,
                   hq=40, hkv=40, head_dim=128, groups=5, fp8_qk=True)
+# Cross-attention to a replicated text K/V prefix at the Wan share: each rank's q holds only its image rows,
+# its k/v shards carry the 512 text rows (the first 226 valid, the padding given as a key mask) in front.
+KV_PREFIX_MASKED = Workload("kv_prefix_masked", 6, batch=1, degree=4, s_local=6820, n_rep=512, rep_first=True,
+                            hq=40, hkv=40, head_dim=128, groups=5,
+                            extra={"kv_only_prefix": True, "text_valid": 226})
 
-ALL = {w.name: w for w in (TINY, WAN_SHARE, WAN_SHARE_G5, JOINT_VARLEN, GQA, E2E_P4)}
+ALL = {w.name: w for w in (TINY, WAN_SHARE, WAN_SHARE_G5, JOINT_VARLEN, GQA, E2E_P4, KV_PREFIX_MASKED)}
 
 
 def randn_bf16(gen: torch.Generator, shape, mult: float = 1.0) -> torch.Tensor:
