@@ -60,10 +60,11 @@
 //    MFMA operand).
 //  * Tiles wholly inside the key gap are skipped; the tail tile and tiles
 //    that straddle the gap are masked per element.
-//  * Steps over clean tiles (no key past the end or in the gap) run in whole
-//    ring rounds with the stages compile-time constants: every LDS read and
-//    tile-load address is then a register plus an immediate, with no address
-//    arithmetic in the step.
+//  * Steps over clean tiles (no key past the end or in the gap, and with a
+//    key mask, runs of consecutive listed tiles whose keys are all valid) run
+//    in whole ring rounds with the stages compile-time constants: every LDS
+//    read and tile-load address is then a register plus an immediate, with no
+//    address arithmetic in the step.
 //  * Under a range split the workgroups are ordered so that each XCD takes a
 //    contiguous block of (range, head) indices, sharing a head's K/V in its
 //    L2.
@@ -185,6 +186,7 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kStages * (C::kKTile + C::kVTile)];
   // Tiles with at least one valid key, in order, when a key mask is given.
   __shared__ unsigned short tile_list[kMaxMaskTiles];
+  static_assert(kMaxMaskTiles <= 0x1000, "tile index in the low 12 bits of a tile-list entry");
   // Per-wave staging of the output rows (128 bytes of each row at a time, rows
   // 144 bytes apart): global stores then write whole lines.
   constexpr int kStgPitch = 144;
@@ -842,9 +844,20 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     int pos = scan[tid] - cnt;
     nseq = scan[kT - 1];
+    // (an entry's bit 15: every key of the tile valid; bit 14: the next tile is
+    // listed too, so the two are consecutive in the sequence, and is not the
+    // ragged last tile, whose rows past the end only the general step's
+    // clamped loads may fetch -- a clean run loads one tile past its blocks)
+    auto tile_valid = [&](int t) {
+      return t < ntiles &&
+             (valid_bits(t * kBN, mask_word(t * kBN)) | valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) != 0u;
+    };
     for (int t = t0; t < t1; ++t)
-      if ((valid_bits(t * kBN, mask_word(t * kBN)) | valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) != 0u)
-        tile_list[pos++] = (unsigned short)t;
+      if (tile_valid(t)) {
+        const bool full = (valid_bits(t * kBN, mask_word(t * kBN)) & valid_bits(t * kBN + 32, mask_word(t * kBN + 32))) == ~0u;
+        const bool link = t + 1 != tail_tile && tile_valid(t + 1);
+        tile_list[pos++] = (unsigned short)(t | (full ? 0x8000 : 0) | (link ? 0x4000 : 0));
+      }
     __syncthreads();
   }
   // Pieces of work: (query tile qtile, positions [p0, p0 + n) of the tile
@@ -908,7 +921,7 @@ void attn_fwd_kernel(AttnArgs a) {
     // (uniform across the workgroup: kept in scalar registers)
     auto seq_tile = [&](int pos) {
       pos += p0;
-      if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
+      if constexpr (MASK) return __builtin_amdgcn_readfirstlane((int)(tile_list[pos] & 0x0FFF));
       else return pos < skip_first ? pos : pos + nskip;
     };
     // Position pos goes to stage pos % kStages; past the end the last tile is
@@ -1019,11 +1032,28 @@ void attn_fwd_kernel(AttnArgs a) {
                   SB, kbb, B0{}, 0, ~0u, false, sA, sB, pA, pB);
         tile_barrier();
       };
-      // Clean steps from step i: the first tile at or after step i's that is
-      // dirty, or the side of the gap ending, ends the run (no key mask: with
-      // one, positions follow the tile list).
+      // Clean steps from step i.  Without a key mask the first tile at or after
+      // step i's that is dirty, or the side of the gap ending, ends the run;
+      // with one the run lasts while the listed tiles are full (every key
+      // valid) and consecutive, so their blocks need no mask either.
       auto clean_run = [&](int i) -> int {
-        if constexpr (MASK) return 0;
+        if constexpr (MASK) {
+          // positions from p0 + i whose tile is full and followed by the next
+          // tile, found 64 at a time by a wave ballot (the same in every wave)
+          const int room = n - 2 - i;
+          if (room <= 0) return 0;
+          const int q = p0 + i;
+          int k = 0;
+          for (;;) {
+            const int p = q + k + (fresh_tid() & 63);
+            const bool ok = p < nseq && (tile_list[p] & 0xC000) == 0xC000;
+            const unsigned long long bad = __ballot(!ok);
+            if (bad != 0ull) { k += __builtin_ctzll(bad); break; }
+            k += 64;
+            if (k > room) break;
+          }
+          return __builtin_amdgcn_readfirstlane(max(0, min(room, k - 1)));
+        }
         const int room = n - 2 - i;   // steps whose tile load stays inside the piece
         const int q = p0 + i;
         int t0, tend;
@@ -1054,15 +1084,14 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int k = 0; k < kKOffs; ++k) kcur[k] += C::kKTile;
         tc = seq_tile(i + rounds * kStages);
         dc = is_dirty(tc);
+        if constexpr (MASK) mw1 = mask_word(tc * kBN + 32);
       };
       for (int i = 0;; ++i) {
-        if constexpr (!MASK) {
-          if (sa == 0) {
-            const int rounds = clean_run(i) / kStages;
-            if (rounds > 0) {
-              run_clean(i, rounds);
-              i += rounds * kStages;
-            }
+        if (sa == 0) {
+          const int rounds = clean_run(i) / kStages;
+          if (rounds > 0) {
+            run_clean(i, rounds);
+            i += rounds * kStages;
           }
         }
         const int sb = sa == kStages - 1 ? 0 : sa + 1;
